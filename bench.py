@@ -1,0 +1,175 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one forward pass (both contractions, online softmax, epilogue) over
+the whole batch of the workload, inputs already resident in HBM. Prints ONE
+JSON line. Throughput is TFLOP/s with FLOPs = 4*B*H*S^2*D, halved under the
+causal mask (for the window+sink workload the nominal causal figure overstates
+the work; the kept-pair count is reported beside it in `config`).
+
+`roofline` describes the forward kernel: achieved = algorithmic FLOPs of one
+launch / mean launch duration (HIP events on the stream the kernel runs on);
+peak = MI355X dense bf16/fp16 MFMA (2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096
+FLOP/clk) or fp32 MFMA (157.3 TFLOP/s). `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload (a few heads, all rows).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=0,
+                    help="heads of the workload the oracle baseline runs (0 = auto)")
+    return ap.parse_args()
+
+
+def nominal_flops(w) -> float:
+    f = 4.0 * w.B * w.H * w.S * w.S * w.D
+    return f / 2.0 if w.causal else f
+
+
+def kept_pairs(w) -> int:
+    S, W, ns = w.S, w.window, w.n_sink
+    if not w.causal:
+        return S * S
+    if W == 0 or W >= S:
+        return S * (S + 1) // 2
+    tot = W * (W + 1) // 2 + (S - W) * W
+    tot += sum(min(ns, i - W + 1) for i in range(W, S))
+    return tot
+
+
+def cpu_baseline(w, q, k, v, n_heads: int):
+    """Time the fp64 oracle on the first n_heads (b, h) heads, all rows."""
+    import numpy as np
+    from oracle import attention as oracle
+    import fa_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
+    arrs = [(fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, h:h + 1]),
+             fa_inputs.to_f64(v[b:b + 1, h:h + 1])) for b, h in heads]
+    t0 = time.perf_counter()
+    for qq, kk, vv in arrs:
+        oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale, window=w.window,
+                             n_sink=w.n_sink)
+    dt = time.perf_counter() - t0
+    flops = nominal_flops(w) * len(heads) / (w.B * w.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} heads (all {w.S} rows each) of the same "
+                      f"workload, fp64 NumPy, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward pass here runs on a single "
+              "MI355X (the multi-GPU sharding is a design note, not built); use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fa_inputs
+    import io_aware_tiled_flash_amd as fa
+
+    name = args.workload or fa_inputs.HEADLINE
+    w = fa_inputs.WORKLOADS[name]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    q, k, v = fa_inputs.make_workload(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.flash_attn_fwd(qd, kd, vd, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                          scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = nominal_flops(w)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    e = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    alg_bytes = 4 * w.B * w.H * w.S * w.D * e + 4 * w.B * w.H * w.S
+
+    out = {
+        "metric": "attention fwd TFLOP/s & % MFMA peak (causal bf16 B4 H16 S4096 D128)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: Q, K, V iid N(0,1), numpy default_rng(seed 0), rounded to dtype",
+        "config": {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": w.causal, "window": w.window, "n_sink": w.n_sink,
+                   "scale": w.scale, "layout": "[B,H,S,D] contiguous",
+                   "flops_per_step": flops, "kept_pairs_per_head": kept_pairs(w),
+                   "frac_of_peak_wall": round(value / peak, 4),
+                   "alg_hbm_bytes_per_step": alg_bytes,
+                   "alg_hbm_GBps": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": f"fa::fa_fwd_{'f32' if w.dtype == 'f32' else 'half'}_kernel",
+                     "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                     "min_launch_us": round(min(launch_ms) * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_heads or max(1, min(w.B * w.H, int(2 ** 26 // (w.S * w.S) * 8)))
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, n)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+/*
+ * flash_attn.h -- C ABI of the MI355X (gfx950) tiled attention forward pass.
+ *
+ * The operation. For every (batch b, head h) and query row i:
+ *
+ *     O[b,h,i,:] = sum_j P[i,j] V[b,h,j,:],   P[i,:] = softmax_j( scale * Q[b,h,i,:].K[b,h,j,:] )
+ *     LSE[b,h,i] = log sum_j exp( scale * Q[b,h,i,:].K[b,h,j,:] )      (natural log)
+ *
+ * with the sums over the keys j the mask keeps. This is ordinary scaled
+ * dot-product attention ("Flash Attention" overview page, "The Problem with
+ * Standard Attention"), computed the way the pages' tiled methods do: a query
+ * row-block streams over key/value blocks, carrying a running max, a running
+ * sum and an output accumulator under the online-softmax rescale (Lab 3 page
+ * "Tiled attention with online softmax"; Lesson 91 deck, slide 11 "Online
+ * softmax: tiled update equations"), and writes O and the logsumexp once,
+ * never forming the S x S score matrix ("Flash Attention" page, "IO-Aware
+ * Algorithm": write the output once at the end).
+ *
+ * Mask (keep(i, j)):
+ *   causal == 0 : every key (window must be 0);
+ *   causal == 1 : j <= i (diagonal kept: the Lab 3 page's lower-triangular
+ *                 mask), and if window > 0 also  (i - j < window  OR  j < n_sink).
+ *   window = width counted in keys including the query itself; window == 0
+ *   means no window; n_sink = number of leading key positions that every
+ *   query may see (the Lab 3 page's exercise on "sink" tokens plus a sliding
+ *   window); n_sink is ignored when window == 0.
+ *
+ * Callers include no HIP header; every pointer is a plain address.
+ */
+#ifndef IO_AWARE_TILED_FLASH_AMD_FLASH_ATTN_H
+#define IO_AWARE_TILED_FLASH_AMD_FLASH_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. lse is always fp32. */
+enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 };
+
+/* Return codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,     /* an argument breaks a precondition; nothing was launched or written */
+  FA_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (head dim, sizes) */
+  FA_ERR_HIP = -3          /* the HIP runtime reported an error while launching */
+};
+
+/*
+ * flash_attn_fwd -- enqueue the attention forward pass on `stream`.
+ *
+ * q, k, v : device pointers, [B, H, S, D] dense row-major (D fastest), element
+ *           type `dtype`, 16-byte aligned. Read only; they may alias each other.
+ * o       : device pointer, [B, H, S, D], `dtype`, 16-byte aligned. Must not
+ *           overlap q, k or v. Every element is written.
+ * lse     : device pointer, [B, H, S] fp32, 4-byte aligned. Every element is
+ *           written: the natural-log logsumexp of the scaled, masked score row.
+ * B, H, S : >= 1.   D : head dimension, one of 16, 32, 64, 128.
+ * causal  : 0 or 1.  window >= 0 (window > 0 needs causal == 1).  n_sink >= 0.
+ * scale   : finite fp32 multiplier of Q.K (used as given: 0 and negative values
+ *           are valid; there is no "default" substitution).
+ * stream  : a hipStream_t, or NULL for the default stream.
+ * dtype   : FA_F32, FA_F16 or FA_BF16.
+ *
+ * Precision: products of the stored inputs, fp32 accumulation; for f16/bf16 the
+ * softmax weights are rounded to the input type (nearest-even) before the
+ * second contraction; O is rounded to `dtype` once, at the end.
+ *
+ * Ownership and timing: the caller owns every buffer. The call validates its
+ * arguments on the host, enqueues one kernel and returns without waiting;
+ * o and lse are valid once `stream` has been synchronised. The library
+ * allocates no device memory and keeps no per-call state; concurrent calls
+ * from several threads are safe.
+ *
+ * Errors: FA_ERR_INVALID (NULL pointer, B/H/S < 1, causal not 0/1, window < 0,
+ * window > 0 with causal == 0, n_sink < 0, non-finite scale, unknown dtype,
+ * misaligned pointer, o overlapping q/k/v, byte sizes overflowing int64),
+ * FA_ERR_UNSUPPORTED (D not in {16,32,64,128}; S, B*H or the grid beyond the
+ * 32-bit index range), FA_ERR_HIP (launch failure). On any error nothing is
+ * enqueued and flash_attn_last_error() describes it.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t S, int64_t D,
+                   int causal, int64_t window, int64_t n_sink, float scale,
+                   void* stream, int dtype);
+
+/*
+ * flash_attn_fwd_counted -- flash_attn_fwd plus an instrumentation counter.
+ *
+ * block_pairs : device pointer to one uint64 (8-byte aligned), or NULL. When
+ *               non-NULL, each work-group atomically adds the number of key/value
+ *               blocks it computed, so after the call the counter has grown by
+ *               the number of (query-block, key-block) tile pairs processed. Blocks
+ *               the mask hides completely are skipped and not counted (the causal
+ *               saving the Lab 3 page's block-pair exercise asks about).
+ * Same arguments, results, errors and timing as flash_attn_fwd otherwise.
+ */
+int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t S, int64_t D,
+                           int causal, int64_t window, int64_t n_sink, float scale,
+                           void* stream, int dtype, uint64_t* block_pairs);
+
+/*
+ * flash_attn_tile_shape -- host-only query of the tile the kernel uses for
+ * (D, dtype): *block_q query rows per work-group and *block_k keys per
+ * streamed key/value block. Returns FA_OK, FA_ERR_INVALID (NULL output,
+ * unknown dtype) or FA_ERR_UNSUPPORTED (D not implemented). Touches no GPU.
+ */
+int flash_attn_tile_shape(int64_t D, int dtype, int* block_q, int* block_k);
+
+/*
+ * flash_attn_last_error -- text of the last error raised on the calling
+ * thread (empty string if none). The pointer stays valid until the thread's
+ * next call into this library.
+ */
+const char* flash_attn_last_error(void);
+
+/* flash_attn_version -- static version string of the library. */
+const char* flash_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IO_AWARE_TILED_FLASH_AMD_FLASH_ATTN_H */

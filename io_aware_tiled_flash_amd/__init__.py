@@ -1,0 +1,153 @@
+"""MI355X (gfx950) tiled online-softmax attention forward pass.
+
+Thin Python binding over the C ABI in include/flash_attn.h (libflashattn.so,
+built in-tree by `io_aware_tiled_flash_amd.build`). Python only marshals
+arguments: torch supplies device memory and the current stream, every step of
+the computation runs in the library's HIP kernels. There is no CPU fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_tile_shape",
+           "flash_attn_last_error", "flash_attn_version", "capi", "library_path",
+           "FA_F32", "FA_F16", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED",
+           "FA_ERR_HIP"]
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
+
+
+class _CAPI:
+    """ctypes view of the exported symbols, with the C names and argument order."""
+
+    def __init__(self, path: str):
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the gfx950 library first "
+                "(python -m io_aware_tiled_flash_amd.build); there is no fallback path")
+        self.lib = ctypes.CDLL(path)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        fwd_args = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i64, f32, vp, i32]
+        self.flash_attn_fwd = self._fn("flash_attn_fwd", fwd_args, i32)
+        self.flash_attn_fwd_counted = self._fn("flash_attn_fwd_counted", fwd_args + [vp], i32)
+        self.flash_attn_tile_shape = self._fn(
+            "flash_attn_tile_shape", [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
+        self.flash_attn_last_error = self._fn("flash_attn_last_error", [], ctypes.c_char_p)
+        self.flash_attn_version = self._fn("flash_attn_version", [], ctypes.c_char_p)
+
+    def _fn(self, name, argtypes, restype):
+        f = getattr(self.lib, name)
+        f.argtypes = argtypes
+        f.restype = restype
+        return f
+
+
+_capi = None
+
+
+def capi() -> _CAPI:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _capi
+    if _capi is None:
+        _capi = _CAPI(library_path)
+    return _capi
+
+
+def flash_attn_last_error() -> str:
+    return capi().flash_attn_last_error().decode()
+
+
+def flash_attn_version() -> str:
+    return capi().flash_attn_version().decode()
+
+
+def flash_attn_tile_shape(D: int, dtype: int) -> tuple[int, int]:
+    """(query rows per work-group, keys per streamed block) for (D, dtype)."""
+    bq, bk = ctypes.c_int(0), ctypes.c_int(0)
+    rc = capi().flash_attn_tile_shape(D, dtype, ctypes.byref(bq), ctypes.byref(bk))
+    _check(rc)
+    return bq.value, bk.value
+
+
+def _check(rc: int):
+    if rc == FA_OK:
+        return
+    msg = flash_attn_last_error()
+    if rc == FA_ERR_INVALID:
+        raise ValueError(msg)
+    if rc == FA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(f"flash_attn error {rc}: {msg}")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D torch tensor [B, H, S, D]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, S, D]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share the shape [B, H, S, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if l.shape != (B, H, S) or l.dtype != torch.float32 or not l.is_contiguous() \
+            or l.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, S] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                B, H, S, D, int(bool(causal)), int(window), int(n_sink), float(scale),
+                stream, _dtype_code(q))
+        if block_pairs is None:
+            rc = capi().flash_attn_fwd(*args)
+        else:
+            if block_pairs.dtype not in (torch.int64, torch.uint64) or block_pairs.numel() < 1 \
+                    or not block_pairs.is_cuda:
+                raise ValueError("block_pairs must be a GPU int64 tensor")
+            rc = capi().flash_attn_fwd_counted(*args, block_pairs.data_ptr())
+    _check(rc)
+    return o, l
+
+
+def flash_attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, n_sink: int = 0,
+                   scale: float | None = None, out=None, lse=None):
+    """Attention forward on the GPU: returns (o [B,H,S,D] in q's dtype, lse [B,H,S] fp32).
+
+    q, k, v: contiguous GPU tensors [B, H, S, D] of one dtype (float32, float16,
+    bfloat16). scale defaults to 1/sqrt(D); window/n_sink need causal=True.
+    Enqueued on torch's current stream; no synchronisation happens here.
+    """
+    return _forward(q, k, v, causal, window, n_sink, scale, out, lse, None)
+
+
+def flash_attn_fwd_counted(q, k, v, block_pairs, *, causal: bool = False, window: int = 0,
+                           n_sink: int = 0, scale: float | None = None, out=None, lse=None):
+    """flash_attn_fwd that also adds the number of (query-block, key-block) tile
+    pairs the kernel computed to block_pairs[0] (a GPU int64 tensor)."""
+    return _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs)

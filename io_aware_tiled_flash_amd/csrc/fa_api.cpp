@@ -1,0 +1,146 @@
+// C ABI of the attention forward pass: host-side validation, normalisation of
+// the mask arguments and dispatch to the gfx950 kernels. See flash_attn.h for
+// the contract.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/flash_attn.h"
+#include "fa_kernel.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case FA_F32: return 4;
+    case FA_F16: return 2;
+    case FA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool supported_d(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+int forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+            int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink, float scale,
+            void* stream, int dtype, uint64_t* block_pairs) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID, "null tensor pointer");
+  if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_INVALID, "B, H and S must be >= 1");
+  if (D < 1) return fail(FA_ERR_INVALID, "D must be >= 1");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1");
+  if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && !causal) return fail(FA_ERR_INVALID, "a sliding window needs causal = 1");
+  if (n_sink < 0) return fail(FA_ERR_INVALID, "n_sink must be >= 0");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
+  const int e = elem_bytes(dtype);
+  if (e == 0) return fail(FA_ERR_INVALID, "unknown dtype");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(FA_ERR_INVALID, "lse must be 4-byte aligned");
+  if (block_pairs && !aligned(block_pairs, 8))
+    return fail(FA_ERR_INVALID, "block_pairs must be 8-byte aligned");
+  // Byte sizes must fit in int64: B*H*S*D*e.
+  const int64_t lim = INT64_MAX;
+  if (B > lim / H) return fail(FA_ERR_INVALID, "B*H overflows");
+  const int64_t bh = B * H;
+  if (bh > lim / S) return fail(FA_ERR_INVALID, "B*H*S overflows");
+  const int64_t rows = bh * S;
+  if (rows > lim / D || rows * D > lim / e) return fail(FA_ERR_INVALID, "tensor size overflows");
+  const uint64_t tbytes = (uint64_t)(rows * D * e);
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
+      overlaps(o, tbytes, v, tbytes))
+    return fail(FA_ERR_INVALID, "o overlaps q, k or v");
+  if (overlaps(lse, (uint64_t)rows * 4, o, tbytes))
+    return fail(FA_ERR_INVALID, "lse overlaps o");
+
+  if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  const int64_t br = fa::tile_rows();
+  const int64_t nqb = (S + br - 1) / br;
+  if (S > INT32_MAX - 2 * br || bh > INT32_MAX || nqb * bh > (int64_t)UINT32_MAX / 256)
+    return fail(FA_ERR_UNSUPPORTED, "S, B*H or the grid exceed the 32-bit index range");
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.block_pairs = reinterpret_cast<unsigned long long*>(block_pairs);
+  p.S = (int)S;
+  p.BH = (int)bh;
+  p.nqb = (int)nqb;
+  p.causal = causal;
+  // A window as wide as the sequence hides nothing: fold it to "no window".
+  p.window = (window >= S) ? 0 : (int)window;
+  p.n_sink = (p.window == 0) ? 0 : (int)(n_sink < S ? n_sink : S);
+  // scores are used as exp2(c * s - m2) with c = |scale| log2(e) > 0; a
+  // negative scale flips the sign of Q instead. A zero scale uses the
+  // smallest normal float, whose products with finite scores round exp2 to
+  // exactly 1, the result of a zero scale, while -inf masked scores stay -inf.
+  double c = std::fabs((double)scale) * 1.4426950408889634;
+  float cf = (float)c;
+  if (!(cf >= FLT_MIN)) cf = FLT_MIN;
+  p.c = cf;
+  p.neg = scale < 0.f ? 1 : 0;
+
+  hipError_t err = fa::launch_fwd(p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                   int64_t H, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
+                   float scale, void* stream, int dtype) {
+  return forward(q, k, v, o, lse, B, H, S, D, causal, window, n_sink, scale, stream, dtype,
+                 nullptr);
+}
+
+int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t window,
+                           int64_t n_sink, float scale, void* stream, int dtype,
+                           uint64_t* block_pairs) {
+  return forward(q, k, v, o, lse, B, H, S, D, causal, window, n_sink, scale, stream, dtype,
+                 block_pairs);
+}
+
+int flash_attn_tile_shape(int64_t D, int dtype, int* block_q, int* block_k) {
+  g_last_error.clear();
+  if (!block_q || !block_k) return fail(FA_ERR_INVALID, "null output pointer");
+  if (elem_bytes(dtype) == 0) return fail(FA_ERR_INVALID, "unknown dtype");
+  if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  *block_q = fa::tile_rows();
+  *block_k = fa::tile_keys();
+  return FA_OK;
+}
+
+const char* flash_attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* flash_attn_version(void) { return "io_aware_tiled_flash_amd 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects every invalid argument before touching the GPU.
+
+No call here reaches a kernel launch: each one fails host-side validation
+(pointers are fake but never dereferenced), so the suite runs without a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+import subprocess
+
+import pytest
+
+import io_aware_tiled_flash_amd as fa
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADERS = sorted((ROOT / "include").glob("*.h"))
+
+# fake but aligned, disjoint "device" addresses; validation never dereferences them
+Q, K, V, O, L = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def _declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\**\s*(flash_attn_\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_headers_declare_the_abi():
+    names = _declared_functions()
+    assert {"flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_tile_shape",
+            "flash_attn_last_error", "flash_attn_version"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    assert pathlib.Path(fa.library_path).exists(), "build the library first"
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = _declared_functions() - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(fa.library_path)
+    for name in _declared_functions():
+        getattr(lib, name)
+
+
+def test_version_and_tile_shape():
+    assert "gfx950" in fa.flash_attn_version()
+    for D in (16, 32, 64, 128):
+        for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
+            bq, bk = fa.flash_attn_tile_shape(D, dt)
+            assert bq >= 32 and bk >= 32 and bq % 32 == 0 and bk % 32 == 0
+    with pytest.raises(NotImplementedError):
+        fa.flash_attn_tile_shape(48, fa.FA_BF16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_tile_shape(64, 7)
+
+
+def _call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, S=64, D=64, causal=0, window=0, n_sink=0,
+          scale=0.125, stream=None, dtype=fa.FA_BF16, counter=None):
+    c = fa.capi()
+    args = (q, k, v, o, lse, B, H, S, D, causal, window, n_sink, scale, stream, dtype)
+    if counter is None:
+        rc = c.flash_attn_fwd(*args)
+    else:
+        rc = c.flash_attn_fwd_counted(*args, counter)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID = {
+    "null_q": dict(q=None),
+    "null_k": dict(k=None),
+    "null_v": dict(v=None),
+    "null_o": dict(o=None),
+    "null_lse": dict(lse=None),
+    "B0": dict(B=0),
+    "H0": dict(H=0),
+    "S0": dict(S=0),
+    "S_negative": dict(S=-5),
+    "D0": dict(D=0),
+    "causal_2": dict(causal=2),
+    "causal_negative": dict(causal=-1),
+    "window_negative": dict(causal=1, window=-1),
+    "window_without_causal": dict(causal=0, window=16),
+    "n_sink_negative": dict(causal=1, window=16, n_sink=-1),
+    "scale_nan": dict(scale=float("nan")),
+    "scale_inf": dict(scale=float("inf")),
+    "scale_neg_inf": dict(scale=float("-inf")),
+    "dtype_unknown": dict(dtype=3),
+    "dtype_negative": dict(dtype=-1),
+    "q_misaligned": dict(q=Q + 8),
+    "k_misaligned": dict(k=K + 2),
+    "v_misaligned": dict(v=V + 4),
+    "o_misaligned": dict(o=O + 8),
+    "lse_misaligned": dict(lse=L + 2),
+    "o_overlaps_q": dict(o=Q + 64),
+    "o_overlaps_v": dict(o=V - 64),
+    "lse_overlaps_o": dict(lse=O + 128),
+    "size_overflow": dict(B=1 << 40, H=1 << 20, S=1 << 10),
+    "counter_misaligned": dict(counter=0x600004),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID))
+def test_invalid_arguments_rejected(case):
+    rc, msg = _call(**INVALID[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+    assert msg
+
+
+@pytest.mark.parametrize("D", [8, 48, 96, 256, 512])
+def test_unsupported_head_dim(D):
+    rc, msg = _call(D=D)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "head dim" in msg
+
+
+def test_index_range_limit():
+    rc, msg = _call(S=1 << 31, D=64, o=1 << 44, lse=1 << 46, v=1 << 42, k=1 << 41, q=1 << 40)
+    assert rc == fa.FA_ERR_UNSUPPORTED, msg
+
+
+def test_error_text_clears_on_success_path_queries():
+    _call(q=None)
+    assert fa.flash_attn_last_error()
+    fa.flash_attn_tile_shape(64, fa.FA_F16)
+    assert fa.flash_attn_last_error() == ""
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(x, x, x)

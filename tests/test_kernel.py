@@ -1,0 +1,270 @@
+"""GPU parity: the gfx950 kernels through the C ABI against the fp64 oracle.
+
+Inputs are seeded (fa_inputs); the oracle reads the very values stored on the
+GPU (exactly upcast to fp64) and its output is not rounded before comparison.
+Bars: max |dO| <= 1e-5 (f32), 4e-3 (f16), 1.6e-2 (bf16); |dLSE| <= 1e-3 *
+max(1, |LSE|).
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import io_aware_tiled_flash_amd as fa
+from oracle import attention as ORACLE
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-5, "f16": 4e-3, "bf16": 1.6e-2}
+TOL_LSE_REL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def gpu_fwd(q, k, v, **kw):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = fa.flash_attn_fwd(qd, kd, vd, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o, lse, q, k, v, dtype, *, causal, scale, window=0, n_sink=0, heads=None,
+            rows=None, label="", tol_o=None):
+    """o, lse: GPU results (device tensors). heads: list of (b, h) to check
+    (default all); rows: query rows to check (default all)."""
+    tol_o = TOL_O[dtype] if tol_o is None else tol_o
+    B, H, S, D = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    worst_o, worst_l = 0.0, 0.0
+    for b, h in heads:
+        q64, k64, v64 = (fa_inputs.to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+        O, L = ORACLE.attention_fwd(q64, k64, v64, causal=causal, scale=scale, window=window,
+                                    n_sink=n_sink, rows=rows)
+        r = slice(None) if rows is None else torch.as_tensor(np.asarray(rows))
+        og = o[b, h].float().cpu()[r].double().numpy()
+        lg = lse[b, h].cpu()[r].double().numpy()
+        assert np.isfinite(og).all() and np.isfinite(lg).all(), label
+        worst_o = max(worst_o, float(np.abs(og - O[0, 0]).max()))
+        worst_l = max(worst_l, float((np.abs(lg - L[0, 0]) / np.maximum(1.0, np.abs(L[0, 0]))).max()))
+    _say(f"  {label}: max|dO|={worst_o:.3e} (tol {tol_o:g})  max rel dLSE={worst_l:.3e}")
+    if os.environ.get("FA_PARITY_LOG"):
+        with open(os.environ["FA_PARITY_LOG"], "a") as f:
+            f.write(f"{label}\t{worst_o:.3e}\t{tol_o:g}\t{worst_l:.3e}\n")
+    assert worst_o <= tol_o, (label, worst_o)
+    assert worst_l <= TOL_LSE_REL, (label, worst_l)
+    return worst_o, worst_l
+
+
+# --------------------------------------------------------------------------- #
+# The five workloads
+# --------------------------------------------------------------------------- #
+
+def _sample_rows(S, rng, n=192):
+    edges = [0, 1, 2, 63, 64, 65, 127, 128, 129, S // 2, S - 129, S - 128, S - 65, S - 64,
+             S - 2, S - 1]
+    rows = set(r for r in edges if 0 <= r < S)
+    rows |= set(rng.choice(S, size=min(n, S), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", list(fa_inputs.WORKLOADS))
+def test_workload_parity(name):
+    w = fa_inputs.WORKLOADS[name]
+    _say(f"workload {name}: generating inputs")
+    q, k, v = fa_inputs.make_workload(w)
+    _say(f"workload {name}: launching")
+    o, lse = gpu_fwd(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink, scale=w.scale)
+    assert o.shape == q.shape and o.dtype == q.dtype and lse.shape == q.shape[:3]
+    small = w.B * w.H * w.S <= 32768
+    if small:
+        compare(o, lse, q, k, v, w.dtype, causal=w.causal, scale=w.scale, window=w.window,
+                n_sink=w.n_sink, label=name)
+    else:
+        rng = np.random.default_rng(1234)
+        heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
+        rows = _sample_rows(w.S, rng)
+        compare(o, lse, q, k, v, w.dtype, causal=w.causal, scale=w.scale, window=w.window,
+                n_sink=w.n_sink, heads=heads, rows=rows, label=name + " (sampled rows)")
+        # properties at full size: every output finite, causal row 0 is V[0]
+        assert torch.isfinite(lse).all()
+        assert torch.isfinite(o.float()).all()
+        if w.causal:
+            assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+
+
+# --------------------------------------------------------------------------- #
+# Ragged lengths, head dims, dtypes, masks
+# --------------------------------------------------------------------------- #
+
+MASKS = [(False, 0, 0), (True, 0, 0), (True, 100, 4), (True, 33, 0), (True, 64, 70)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_ragged_lengths(dtype, D):
+    for S in (1, 7, 63, 65, 127, 129, 200, 1000):
+        q, k, v = fa_inputs.make_qkv(1, 2, S, D, dtype, seed=S + D)
+        for causal, window, n_sink in MASKS:
+            scale = 1.0 / math.sqrt(D)
+            o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
+            compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                    n_sink=n_sink, label=f"{dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_multi_batch_head_layout(dtype):
+    """B and H index distinct heads: B=3, H=5, ragged S."""
+    q, k, v = fa_inputs.make_qkv(3, 5, 300, 64, dtype, seed=7)
+    for causal in (False, True):
+        o, lse = gpu_fwd(q, k, v, causal=causal, scale=0.125)
+        compare(o, lse, q, k, v, dtype, causal=causal, scale=0.125, label=f"{dtype} B3H5 c{causal}")
+
+
+# --------------------------------------------------------------------------- #
+# Stress inputs and degenerate cases
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_sharp_softmax_and_key_offset(dtype):
+    """Q x 8 gives nearly one-hot rows (large rescales); a common key offset
+    shifts every score of a row by the same amount (O unchanged)."""
+    q, k, v = fa_inputs.make_qkv(1, 2, 520, 128, dtype, seed=3)
+    tdt = q.dtype
+    q8 = (q.float() * 8).to(tdt)
+    o, lse = gpu_fwd(q8, k, v, causal=True, scale=1 / math.sqrt(128))
+    # In fp32 the scores themselves carry a rounding error of order
+    # eps32 * |s| * sqrt(D); scaling Q by 8 scales that error, and so the
+    # error of every softmax weight, by 8, so the fp32 bar scales with it.
+    # (For f16/bf16 the bar is set by rounding P and O to 8-/11-bit
+    # mantissas, which does not grow with the score magnitude.)
+    tol = TOL_O[dtype] * 8 if dtype == "f32" else None
+    compare(o, lse, q8, k, v, dtype, causal=True, scale=1 / math.sqrt(128), label=f"{dtype} Qx8",
+            tol_o=tol)
+    off = torch.from_numpy(np.random.default_rng(0).standard_normal(128).astype(np.float32) * 4)
+    k2 = (k.float() + off).to(tdt)
+    o2, lse2 = gpu_fwd(q, k2, v, causal=True, scale=1 / math.sqrt(128))
+    compare(o2, lse2, q, k2, v, dtype, causal=True, scale=1 / math.sqrt(128),
+            label=f"{dtype} key offset")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_scale_zero_and_negative(dtype):
+    """scale = 0: every visible key weighs the same (O = mean of visible V,
+    LSE = ln count). A negative scale is a valid multiplier too."""
+    q, k, v = fa_inputs.make_qkv(1, 2, 150, 64, dtype, seed=11)
+    for causal, window, n_sink in MASKS:
+        for scale in (0.0, -0.2):
+            o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
+            compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                    n_sink=n_sink, label=f"{dtype} scale={scale} c{causal} w{window}")
+
+
+def test_window_one_and_wide_window():
+    """window = 1 without sinks: each row sees only itself (O = V exactly);
+    a window wider than S is plain causal."""
+    q, k, v = fa_inputs.make_qkv(1, 3, 257, 128, "bf16", seed=5)
+    o, lse = gpu_fwd(q, k, v, causal=True, window=1, scale=0.1)
+    assert torch.equal(o.cpu(), v)
+    o1, l1 = gpu_fwd(q, k, v, causal=True, window=0, scale=0.1)
+    o2, l2 = gpu_fwd(q, k, v, causal=True, window=5000, n_sink=3, scale=0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_self_attention_aliasing_and_side_stream():
+    """q, k and v may be one tensor; the launch follows torch's current stream."""
+    x, _, _ = fa_inputs.make_qkv(2, 4, 333, 64, "f16", seed=9)
+    xd = x.cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.flash_attn_fwd(xd, xd, xd, causal=True, scale=0.125)
+    s.synchronize()
+    compare(o, lse, x, x, x, "f16", causal=True, scale=0.125, label="aliased q=k=v, side stream")
+
+
+def test_preallocated_outputs_fully_written():
+    q, k, v = fa_inputs.make_qkv(1, 2, 77, 32, "bf16", seed=2)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((1, 2, 77), float("nan"), device="cuda")
+    fa.flash_attn_fwd(qd, kd, vd, causal=True, out=out, lse=lse, scale=0.3)
+    torch.cuda.synchronize()
+    compare(out, lse, q, k, v, "bf16", causal=True, scale=0.3, label="preallocated outputs")
+
+
+def test_deterministic_bitwise():
+    q, k, v = fa_inputs.make_qkv(2, 4, 1000, 128, "bf16", seed=4)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    ref = fa.flash_attn_fwd(qd, kd, vd, causal=True, window=300, n_sink=4)
+    for _ in range(10):
+        o, l = fa.flash_attn_fwd(qd, kd, vd, causal=True, window=300, n_sink=4)
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
+# --------------------------------------------------------------------------- #
+# Block skipping: the instrumentation counter against a count from the mask
+# --------------------------------------------------------------------------- #
+
+def _pairs_with_visible_keys(S, bq, bk, causal, window, n_sink):
+    total = 0
+    for q0 in range(0, S, bq):
+        rows = np.arange(q0, min(S, q0 + bq))
+        keep = ORACLE.visible(rows, S, causal, window, n_sink)
+        for k0 in range(0, S, bk):
+            total += bool(keep[:, k0:k0 + bk].any())
+    return total
+
+
+@pytest.mark.parametrize("S,causal,window,n_sink", [
+    (64, True, 0, 0), (4096, True, 0, 0), (4096, False, 0, 0), (1000, True, 0, 0),
+    (8192, True, 1024, 4), (3000, True, 200, 70), (3000, True, 200, 0)])
+def test_block_pairs_visited(S, causal, window, n_sink):
+    D = 128
+    bq, bk = fa.flash_attn_tile_shape(D, fa.FA_BF16)
+    q, k, v = fa_inputs.make_qkv(1, 1, S, D, "bf16", seed=1)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    fa.flash_attn_fwd_counted(qd, kd, vd, cnt, causal=causal, window=window, n_sink=n_sink)
+    torch.cuda.synchronize()
+    want = _pairs_with_visible_keys(S, bq, bk, causal, window, n_sink)
+    nq, nk = -(-S // bq), -(-S // bk)
+    _say(f"  S={S} causal={causal} w={window} sinks={n_sink}: visited {int(cnt.item())} "
+         f"of {nq * nk} tile pairs (mask-derived {want})")
+    assert int(cnt.item()) == want
+
+
+def test_invalid_arguments_raise_before_launch():
+    q, k, v = (t.cuda() for t in fa_inputs.make_qkv(1, 1, 16, 64, "bf16"))
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, k, v, causal=False, window=4)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, k, v, scale=float("nan"))
+    with pytest.raises(NotImplementedError):
+        x = torch.zeros(1, 1, 16, 48, dtype=torch.bfloat16, device="cuda")
+        fa.flash_attn_fwd(x, x, x)
+
+
+def test_tiled_block_guide_example_fp32():
+    """The NumPy tiled-block guide's validation case (non-causal, N=512,
+    d=64, seed 42, fp32) through the fp32 path, within its asserted 1e-4."""
+    rng = np.random.default_rng(42)
+    arrs = [rng.normal(size=(512, 64)).astype(np.float32) for _ in range(3)]
+    q, k, v = (torch.from_numpy(a).reshape(1, 1, 512, 64) for a in arrs)
+    o, lse = gpu_fwd(q, k, v, causal=False, scale=0.125)
+    worst, _ = compare(o, lse, q, k, v, "f32", causal=False, scale=0.125, label="guide fp32")
+    assert worst < 1e-4
