@@ -40,7 +40,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,
                     help="heads of the workload the oracle baseline runs (0 = auto)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB, --steps times "
+                         "(calibrates the HBM byte counters against a known size)")
     return ap.parse_args()
+
+
+def copy_probe(mib: int, steps: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read_per_launch": n * 4,
+                      "copy_probe_bytes_written_per_launch": n * 4, "launches": steps}))
+
+
+def kernel_name(fa, w) -> str:
+    code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w.dtype]
+    bq, bk = fa.flash_attn_tile_shape(w.B, w.H, w.S, w.D, code)
+    if w.dtype != "f32" and w.D in (64, 128):
+        return f"fa::fa_fwd_fast_kernel<{w.dtype},D={w.D},waves={bq // 32}> ({bq}x{bk} tile)"
+    return f"fa::fa_fwd_{'f32' if w.dtype == 'f32' else 'half'}_kernel<D={w.D}> ({bq}x{bk} tile)"
 
 
 def nominal_flops(w) -> float:
@@ -90,6 +113,10 @@ def main():
               "MI355X (the multi-GPU sharding is a design note, not built); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
 
     import torch
     import fa_inputs
@@ -160,7 +187,7 @@ def main():
                    "alg_hbm_GBps": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": f"fa::fa_fwd_{'f32' if w.dtype == 'f32' else 'half'}_kernel",
+                     "kernel": kernel_name(fa, w),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,

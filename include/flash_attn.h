@@ -102,12 +102,16 @@ int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o,
                            void* stream, int dtype, uint64_t* block_pairs);
 
 /*
- * flash_attn_tile_shape -- host-only query of the tile the kernel uses for
- * (D, dtype): *block_q query rows per work-group and *block_k keys per
- * streamed key/value block. Returns FA_OK, FA_ERR_INVALID (NULL output,
- * unknown dtype) or FA_ERR_UNSUPPORTED (D not implemented). Touches no GPU.
+ * flash_attn_tile_shape -- host-only query of the tile flash_attn_fwd uses for
+ * a problem of this shape: *block_q query rows per work-group and *block_k keys
+ * per streamed key/value block (the kernel and its work-group size are chosen
+ * from B*H, S, D and dtype). Returns FA_OK, FA_ERR_INVALID (NULL output,
+ * B/H/S < 1, unknown dtype) or FA_ERR_UNSUPPORTED (D not implemented).
+ * Touches no GPU. The environment variable FLASH_ATTN_WAVES=4|8, if set,
+ * overrides the work-group size of the bf16/f16 D=64/128 kernel (tuning aid).
  */
-int flash_attn_tile_shape(int64_t D, int dtype, int* block_q, int* block_k);
+int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,
+                          int* block_k);
 
 /*
  * flash_attn_last_error -- text of the last error raised on the calling

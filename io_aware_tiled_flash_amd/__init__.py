@@ -37,7 +37,8 @@ class _CAPI:
         self.flash_attn_fwd = self._fn("flash_attn_fwd", fwd_args, i32)
         self.flash_attn_fwd_counted = self._fn("flash_attn_fwd_counted", fwd_args + [vp], i32)
         self.flash_attn_tile_shape = self._fn(
-            "flash_attn_tile_shape", [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
+            "flash_attn_tile_shape",
+            [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
         self.flash_attn_last_error = self._fn("flash_attn_last_error", [], ctypes.c_char_p)
         self.flash_attn_version = self._fn("flash_attn_version", [], ctypes.c_char_p)
 
@@ -67,10 +68,11 @@ def flash_attn_version() -> str:
     return capi().flash_attn_version().decode()
 
 
-def flash_attn_tile_shape(D: int, dtype: int) -> tuple[int, int]:
-    """(query rows per work-group, keys per streamed block) for (D, dtype)."""
+def flash_attn_tile_shape(B: int, H: int, S: int, D: int, dtype: int) -> tuple[int, int]:
+    """(query rows per work-group, keys per streamed block) flash_attn_fwd uses
+    for a [B, H, S, D] problem of this dtype."""
     bq, bk = ctypes.c_int(0), ctypes.c_int(0)
-    rc = capi().flash_attn_tile_shape(D, dtype, ctypes.byref(bq), ctypes.byref(bk))
+    rc = capi().flash_attn_tile_shape(B, H, S, D, dtype, ctypes.byref(bq), ctypes.byref(bk))
     _check(rc)
     return bq.value, bk.value
 

@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflashattn.so")
-SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_fwd_fast.hip"),
+           os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "../../include/flash_attn.h"
@@ -73,7 +74,8 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
     return fail(FA_ERR_INVALID, "lse overlaps o");
 
   if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
-  const int64_t br = fa::tile_rows();
+  const fa::Plan plan = fa::plan_fwd(B * H, S, D, dtype);
+  const int64_t br = plan.block_q;
   const int64_t nqb = (S + br - 1) / br;
   if (S > INT32_MAX - 2 * br || bh > INT32_MAX || nqb * bh > (int64_t)UINT32_MAX / 256)
     return fail(FA_ERR_UNSUPPORTED, "S, B*H or the grid exceed the 32-bit index range");
@@ -102,7 +104,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.c = cf;
   p.neg = scale < 0.f ? 1 : 0;
 
-  hipError_t err = fa::launch_fwd(p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
+  hipError_t err = fa::launch_plan(plan, p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
     return FA_ERR_HIP;
@@ -111,6 +113,40 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
 }
 
 }  // namespace
+
+namespace fa {
+
+// Kernel choice. bf16/f16 with D = 64 or 128 take the fast kernel; its
+// work-group holds 8 waves (256 query rows share each K/V tile) when that
+// still yields at least two work-groups per CU (256 CUs), else 4 waves.
+// FLASH_ATTN_WAVES=4|8 overrides the wave count (tuning only).
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype) {
+  Plan pl;
+  if (fast_supported((int)D, dtype)) {
+    pl.fast = true;
+    const int64_t wgs8 = BH * ((S + 255) / 256);
+    pl.nw = wgs8 >= 512 ? 8 : 4;
+    if (const char* e = std::getenv("FLASH_ATTN_WAVES")) {
+      const int v = std::atoi(e);
+      if (v == 4 || v == 8) pl.nw = v;
+    }
+    pl.block_q = 32 * pl.nw;
+    pl.block_k = fast_tile_keys();
+  } else {
+    pl.fast = false;
+    pl.nw = 4;
+    pl.block_q = generic_tile_rows();
+    pl.block_k = generic_tile_keys();
+  }
+  return pl;
+}
+
+hipError_t launch_plan(const Plan& plan, const FwdParams& p, int D, int dtype, hipStream_t st) {
+  if (plan.fast) return launch_fast(p, D, dtype, plan.nw, st);
+  return launch_generic(p, D, dtype, st);
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -129,13 +165,17 @@ int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o,
                  block_pairs);
 }
 
-int flash_attn_tile_shape(int64_t D, int dtype, int* block_q, int* block_k) {
+int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,
+                          int* block_k) {
   g_last_error.clear();
   if (!block_q || !block_k) return fail(FA_ERR_INVALID, "null output pointer");
+  if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_INVALID, "B, H and S must be >= 1");
   if (elem_bytes(dtype) == 0) return fail(FA_ERR_INVALID, "unknown dtype");
   if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
-  *block_q = fa::tile_rows();
-  *block_k = fa::tile_keys();
+  if (B > INT64_MAX / H) return fail(FA_ERR_INVALID, "B*H overflows");
+  const fa::Plan plan = fa::plan_fwd(B * H, S, D, dtype);
+  *block_q = plan.block_q;
+  *block_k = plan.block_k;
   return FA_OK;
 }
 

@@ -1,0 +1,119 @@
+// Device-side helpers shared by the attention forward kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernel.h"
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ------------------------------------------------------------------------ //
+// 16-bit element types: MFMA 32x32x16 and packed conversion from fp32.
+// ------------------------------------------------------------------------ //
+template <typename T> struct Half16;
+template <> struct Half16<__bf16> {
+  using v8 = bf16x8;
+  using v2 = bf16x2;
+  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Half16<_Float16> {
+  using v8 = f16x8;
+  using v2 = f16x2;
+  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Two fp32 -> two T (round to nearest even), packed lo | hi << 16, as one
+// packed conversion.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typename Half16<T>::v2 v = {(T)lo, (T)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max / sum of x[lane] and x[lane ^ 32] via v_permlane32_swap.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Visible-key test of the mask (see flash_attn.h), written without
+// short-circuit branches so it lowers to compares and one v_cndmask.
+__device__ __forceinline__ bool keep_ij(int i, int j, int S, int causal, int window, int n_sink) {
+  const bool in_range = j < S;
+  const bool in_window = (window == 0) | ((i - j) < window) | (j < n_sink);
+  return in_range & ((causal == 0) | ((j <= i) & in_window));
+}
+
+// Key-block range a query block [q_lo, q_lo + BR) visits: sink blocks
+// [0, n_sinkb) then [kb_lo, kb_hi]. Blocks outside hold no key visible to
+// any of its rows, so they are never loaded.
+struct BlockRange {
+  int n_sinkb, kb_lo, kb_hi;
+  __device__ __forceinline__ int count() const { return n_sinkb + (kb_hi - kb_lo + 1); }
+  __device__ __forceinline__ int kb(int it) const { return it < n_sinkb ? it : kb_lo + (it - n_sinkb); }
+};
+
+template <int BR, int BC>
+__device__ __forceinline__ BlockRange block_range(int q_lo, int S, int causal, int window, int n_sink) {
+  BlockRange r;
+  r.n_sinkb = 0;
+  r.kb_lo = 0;
+  if (causal) {
+    const int q_last = min(q_lo + BR, S) - 1;
+    r.kb_hi = q_last / BC;
+    if (window > 0) {
+      r.kb_lo = max(0, q_lo - window + 1) / BC;
+      r.n_sinkb = min(r.kb_lo, (n_sink + BC - 1) / BC);
+    }
+  } else {
+    r.kb_hi = (S - 1) / BC;
+  }
+  return r;
+}
+
+// True when every (query row of the block, key of the K block) pair is visible.
+template <int BR, int BC>
+__device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, int window, int n_sink) {
+  bool full = (k0 + BC <= S);
+  if (causal) {
+    full = full && (k0 + BC - 1 <= q_lo);
+    if (window > 0) full = full && ((q_lo + BR - 1 - k0 < window) || (k0 + BC <= n_sink));
+  }
+  return full;
+}
+
+// Work-group -> (query block, batch*head). Heaviest query blocks first under
+// the causal mask; consecutive ids walk over heads so that, with B*H a
+// multiple of 8, every query block of a head runs on the same XCD (the
+// dispatcher deals work-group ids round-robin over the 8 XCDs).
+__device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
+  const int id = blockIdx.x;
+  bh = id % p.BH;
+  const int rank = id / p.BH;
+  qb = p.causal ? (p.nqb - 1 - rank) : rank;
+}
+
+}  // namespace fa

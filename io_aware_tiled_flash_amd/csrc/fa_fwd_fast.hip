@@ -1,0 +1,342 @@
+// Fast tiled online-softmax attention forward pass for gfx950: bf16 / f16,
+// head dim 64 or 128.
+//
+// Same algorithm as the generic kernels (Lab 3 page "Tiled attention with
+// online softmax"; Lesson 91 deck, slide 11): a query block streams over
+// key/value blocks under the online-softmax rescale and writes O / l and the
+// logsumexp once. What differs is how the tiles reach the matrix cores:
+//
+//  * K and V tiles go HBM -> LDS with direct-to-LDS loads
+//    (global_load_lds_dwordx4): no staging registers, no VALU. Each wave
+//    fills a contiguous 1 KiB run of LDS per instruction, so the XOR
+//    swizzle of the LDS layout is applied on the global-address side.
+//  * K is stored row-major with its 16-byte chunks XOR-swizzled by row, so
+//    the 32 lanes reading one chunk column of 32 keys (the A operand of
+//    S^T = K Q^T on v_mfma_f32_32x32x16) hit distinct LDS banks.
+//  * V is stored row-major (no transpose on the way in) with its 64-byte
+//    segments XOR-swizzled by row. The A operand of O^T = V^T P^T needs, per
+//    lane, 8 keys of one column d; ds_read_b64_tr_b16 delivers exactly that:
+//    in each group of 16 lanes, lane o receives element o%4 of the rows that
+//    lanes o/4 + 4k fetched, so lanes fetching V[key0 + r/4][d0 + 4(r%4)..]
+//    leave V[key0 + k][d0 + o] in lane o. Two such reads give 8 keys.
+//  * P never leaves registers: the S^T accumulator, rounded to the input
+//    type, is the B operand of the PV MFMA (key = contraction index, both
+//    operands enumerate the keys of a 16-key chunk in the same order).
+//  * Lazy rescale: a row's running max only moves (and O, l are only
+//    rescaled) when the new block max exceeds it by more than 2^8 in the
+//    base-2 exponent; otherwise the stale max is kept and exp2 arguments stay
+//    <= 8. The result O / l is unchanged by the choice of reference max, and
+//    fp32 holds the <= 256x larger partial sums without loss. The decision is
+//    wave-uniform, so the 64-multiply rescale of O is skipped as a branch.
+//  * Masks are applied only to partially visible blocks, with per-lane
+//    bounds and compile-time key offsets (two VALU ops per score).
+//  * K/V are double-buffered: block it+1 is in flight into the other buffer
+//    while block it is computed; one barrier per block.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_kernel.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBCf = 64;   // keys per streamed block
+constexpr float kTau = 8.f;  // lazy-rescale threshold (base-2 exponent)
+
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS element offset of K[row][chunk*8] (16-byte chunks swizzled by row).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// 64-byte segment swizzle of the V layout.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? (row & 3) : ((row >> 1) & 1);
+}
+
+// Direct HBM -> LDS copy of one BC x D tile (K if IS_V is false, else V).
+// Wave w fills LDS 16-byte positions [w*NI*64, (w+1)*NI*64); position pos is
+// (row, physical chunk) = divmod(pos, D/8) and receives the logical chunk the
+// swizzle maps there. Rows past the sequence end re-read row S-1 (finite
+// data; every such key is masked out).
+template <int D, int NW, bool IS_V, typename T>
+__device__ __forceinline__ void tile_to_lds(T* lds_tile, const T* __restrict__ g, int k0, int S,
+                                            int wave, int lane) {
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int NI = kBCf * CPR / (64 * NW);    // instructions per wave
+#pragma unroll
+  for (int n = 0; n < NI; ++n) {
+    const int base = (wave * NI + n) * 64;
+    const int pos = base + lane;
+    const int row = pos / CPR;
+    const int pc = pos % CPR;
+    int d;
+    if (IS_V) {
+      const int seg = (pc >> 2) ^ v_swz<D>(row);
+      d = 32 * seg + 8 * (pc & 3);
+    } else {
+      d = 8 * (pc ^ k_swz<D>(row));
+    }
+    const int grow = min(k0 + row, S - 1);
+    const T* src = g + (size_t)grow * D + d;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (lds_void*)(lds_tile + base * 8), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x2 lds_tr_read(const T* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_fast_kernel(FwdParams p) {
+  using Tr = Half16<T>;
+  using v8 = typename Tr::v8;
+  constexpr int BR = 32 * NW;
+  constexpr int BC = kBCf;
+  constexpr int NT = BC / 32;     // 32-key sub-tiles
+  constexpr int NDT = D / 32;     // 32-wide d tiles of O^T
+  constexpr int NS = D / 16;      // k-steps of QK^T
+  constexpr int TILE = BC * D;    // elements per K or V tile
+
+  __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  int qb, bh;
+  wg_coords(p, qb, bh);
+  const int S = p.S;
+  const int q_lo = qb * BR;
+  const int i = q_lo + 32 * wave + col;   // this lane's query row
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + head;
+
+  const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
+  const int n_iter = br.count();
+  if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
+
+  // Block 0 in flight while Q is fetched.
+  tile_to_lds<D, NW, false>(&lds[0][0][0], Kh, br.kb(0) * BC, S, wave, lane);
+  tile_to_lds<D, NW, true>(&lds[0][1][0], Vh, br.kb(0) * BC, S, wave, lane);
+
+  // Q fragment (B operand of S^T = K Q^T): lane holds Q[i][16 s + 8 h .. +7].
+  v8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (i < S) w = *reinterpret_cast<const u32x4*>(Qh + (size_t)i * D + 16 * s + 8 * h);
+    if (p.neg) w ^= 0x80008000u;
+    qf[s] = __builtin_bit_cast(v8, w);
+  }
+
+  // Per-lane LDS offsets (elements) of the K fragment (A of S^T) for each
+  // k-step s, relative to the 32-key sub-tile base.
+  int koff[NS];
+  {
+    const int sw = k_swz<D>(col);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) koff[s] = col * D + (((2 * s + h) ^ sw) << 3);
+  }
+  // Per-lane LDS offsets of the V^T fragment (A of O^T) transposed reads.
+  const int r16 = lane & 15;
+  const int grp = (lane >> 4) & 1;
+  const int vsw = D == 128 ? ((r16 >> 2) & 3) : ((r16 >> 3) & 1);
+  const int vbase = (4 * h + (r16 >> 2)) * D + 16 * grp + 4 * (r16 & 3);
+  int vdt[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) vdt[dt] = vbase + ((dt ^ vsw) << 5);
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = kNegInf;   // running max (raw sign-folded score units)
+  float mc = 0.f;          // m_run * c, or 0 while nothing is visible
+  float l = 0.f;           // this lane half's running sum
+  const float c = p.c;
+  const float tau_raw = kTau / c;
+
+  wait_vmem_all();
+  __syncthreads();
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    const int k0 = br.kb(it) * BC;
+    if (it + 1 < n_iter) {
+      const int k1 = br.kb(it + 1) * BC;
+      tile_to_lds<D, NW, false>(&lds[buf ^ 1][0][0], Kh, k1, S, wave, lane);
+      tile_to_lds<D, NW, true>(&lds[buf ^ 1][1][0], Vh, k1, S, wave, lane);
+    }
+    const T* Ks = &lds[buf][0][0];
+    const T* Vs = &lds[buf][1][0];
+
+    // S^T = K Q^T
+    f32x16 sacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        v8 a = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Ks + 32 * t * D + koff[s]));
+        sacc[t] = Tr::mma(a, qf[s], sacc[t]);
+      }
+    }
+
+    // Mask partially visible blocks: key j = k0 + 4h + e, e = 32t + 8g + r.
+    if (!block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink)) {
+      const int jb = k0 + 4 * h;
+      const int hi = (p.causal ? min(i, S - 1) : S - 1) - jb;
+      if (p.window > 0) {
+        const int lo = i - p.window + 1 - jb;
+        const int sk = p.n_sink - 1 - jb;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 32 * t + 8 * (r >> 2) + (r & 3);
+            const bool keep = (e <= hi) & ((e >= lo) | (e <= sk));
+            sacc[t][r] = keep ? sacc[t][r] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int e = 32 * t + 8 * (r >> 2) + (r & 3);
+            sacc[t][r] = (e <= hi) ? sacc[t][r] : kNegInf;
+          }
+      }
+    }
+
+    // Online softmax with lazy rescale.
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mt = fmaxf(mt, sacc[t][r]);
+    mt = xhalf_max(mt);
+    const float m_new = fmaxf(m_run, mt);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + tau_raw)) {
+      const float mc_new = (m_new == kNegInf) ? 0.f : m_new * c;
+      const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
+      m_run = m_new;
+      mc = mc_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    v8 pb[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(__builtin_fmaf(sacc[t][r], c, -mc));
+        sacc[t][r] = e;
+        l += e;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 w;
+        w[0] = pack2<T>(sacc[t][8 * u + 0], sacc[t][8 * u + 1]);
+        w[1] = pack2<T>(sacc[t][8 * u + 2], sacc[t][8 * u + 3]);
+        w[2] = pack2<T>(sacc[t][8 * u + 4], sacc[t][8 * u + 5]);
+        w[3] = pack2<T>(sacc[t][8 * u + 6], sacc[t][8 * u + 7]);
+        pb[t][u] = __builtin_bit_cast(v8, w);
+      }
+    }
+
+    // O^T += V^T P^T; the V^T fragment comes from two transposed LDS reads.
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const T* vk = Vs + (32 * t + 16 * u) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x2 lo = lds_tr_read(vk + vdt[dt]);
+          const u32x2 hi = lds_tr_read(vk + 8 * D + vdt[dt]);
+          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[dt] = Tr::mma(__builtin_bit_cast(v8, w), pb[t][u], oacc[dt]);
+        }
+      }
+
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  // Epilogue: O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
+  const float l_tot = xhalf_sum(l);
+  if (i < S) {
+    const float inv = 1.f / l_tot;
+    T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head + (size_t)i * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        u32x2 w;
+        w[0] = pack2<T>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+        w[1] = pack2<T>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(Oh + d) = w;
+      }
+    if (h == 0) p.lse[(size_t)bh * S + i] = (mc + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------------ //
+// Host side.
+// ------------------------------------------------------------------------ //
+bool fast_supported(int D, int dtype) {
+  return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
+}
+int fast_tile_keys() { return kBCf; }
+
+template <typename T, int D>
+static hipError_t launch_fast_t(const FwdParams& p, int nw, hipStream_t st) {
+  const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH;
+  if (nw == 8)
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8>), dim3(grid), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 4>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast(const FwdParams& p, int D, int dtype, int nw, hipStream_t st) {
+  if (dtype == kDtypeBF16) {
+    if (D == 128) return launch_fast_t<__bf16, 128>(p, nw, st);
+    if (D == 64) return launch_fast_t<__bf16, 64>(p, nw, st);
+  } else if (dtype == kDtypeF16) {
+    if (D == 128) return launch_fast_t<_Float16, 128>(p, nw, st);
+    if (D == 64) return launch_fast_t<_Float16, 64>(p, nw, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

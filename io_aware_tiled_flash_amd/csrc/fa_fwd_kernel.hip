@@ -37,112 +37,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_kernel.h"
 
 namespace fa {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
+namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBR = 32 * kWaves;   // query rows per work-group
 constexpr int kBC = 64;            // keys per streamed block
-constexpr float kNegInf = -__builtin_inff();
-
-// ------------------------------------------------------------------------ //
-// Element-type traits.
-// ------------------------------------------------------------------------ //
-template <typename T> struct Half16;
-template <> struct Half16<__bf16> {
-  using v8 = bf16x8;
-  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Half16<_Float16> {
-  using v8 = f16x8;
-  static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <typename T> __device__ __forceinline__ uint32_t bits16(T x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, x);
-}
-// Two fp32 -> two T (round to nearest even), packed lo | hi << 16.
-template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return bits16<T>((T)lo) | (bits16<T>((T)hi) << 16);
-}
-
-__device__ __forceinline__ float xhalf_max(float x) {
-  // max(x[lane], x[lane ^ 32]) via v_permlane32_swap.
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Visible-key test of the mask (see flash_attn.h), written without
-// short-circuit branches so it lowers to compares and one v_cndmask.
-__device__ __forceinline__ bool keep_ij(int i, int j, int S, int causal, int window, int n_sink) {
-  const bool in_range = j < S;
-  const bool in_window = (window == 0) | ((i - j) < window) | (j < n_sink);
-  return in_range & ((causal == 0) | ((j <= i) & in_window));
-}
-
-// Key-block range a query block visits: sink blocks [0, n_sinkb) then
-// [kb_lo, kb_hi]. Blocks outside hold no key visible to any of its rows.
-struct BlockRange {
-  int n_sinkb, kb_lo, kb_hi;
-  __device__ __forceinline__ int count() const { return n_sinkb + (kb_hi - kb_lo + 1); }
-  __device__ __forceinline__ int kb(int it) const { return it < n_sinkb ? it : kb_lo + (it - n_sinkb); }
-};
-
-__device__ __forceinline__ BlockRange block_range(int q_lo, int S, int causal, int window, int n_sink) {
-  BlockRange r;
-  r.n_sinkb = 0;
-  r.kb_lo = 0;
-  if (causal) {
-    int q_last = min(q_lo + kBR, S) - 1;
-    r.kb_hi = q_last / kBC;
-    if (window > 0) {
-      r.kb_lo = max(0, q_lo - window + 1) / kBC;
-      r.n_sinkb = min(r.kb_lo, (n_sink + kBC - 1) / kBC);
-    }
-  } else {
-    r.kb_hi = (S - 1) / kBC;
-  }
-  return r;
-}
-
-// True when every (query row of the block, key of the K block) pair is visible.
-__device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, int window, int n_sink) {
-  bool full = (k0 + kBC <= S);
-  if (causal) {
-    full = full && (k0 + kBC - 1 <= q_lo);
-    if (window > 0) full = full && ((q_lo + kBR - 1 - k0 < window) || (k0 + kBC <= n_sink));
-  }
-  return full;
-}
-
-// Work-group -> (query block, batch*head). Heaviest query blocks first under
-// the causal mask; consecutive ids walk over heads so that, with B*H a
-// multiple of 8, every query block of a head runs on the same XCD.
-__device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
-  int id = blockIdx.x;
-  bh = id % p.BH;
-  int rank = id / p.BH;
-  qb = p.causal ? (p.nqb - 1 - rank) : rank;
-}
+}  // namespace
 
 // ------------------------------------------------------------------------ //
 // Online-softmax update for one K block, shared by both element paths.
@@ -238,7 +143,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     qf[s] = __builtin_bit_cast(v8, w);
   }
 
-  const BlockRange br = block_range(q_lo, S, p.causal, p.window, p.n_sink);
+  const BlockRange br = block_range<kBR, kBC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_iter = br.count();
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
 
@@ -339,7 +244,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
-    const bool full = block_full(q_lo, k0, S, p.causal, p.window, p.n_sink);
+    const bool full = block_full<kBR, kBC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
     const float alpha = softmax_step<NT>(sacc, full, i, k0, h, p, m2, l);
 
 #pragma unroll
@@ -394,7 +299,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           *reinterpret_cast<u32x2*>(Oh + d) = w;
         }
       }
-    if (h == 0) p.lse[(size_t)bh * S + i] = (m2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (h == 0) p.lse[(size_t)bh * S + i] = (m2 + fast_log2(l_tot)) * kLn2;
   }
 }
 
@@ -453,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
     for (int e = 0; e < 4; ++e) qf[4 * s4 + e] = w[e];
   }
 
-  const BlockRange br = block_range(q_lo, S, p.causal, p.window, p.n_sink);
+  const BlockRange br = block_range<kBR, kBC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_iter = br.count();
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
 
@@ -542,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
       }
     }
 
-    const bool full = block_full(q_lo, k0, S, p.causal, p.window, p.n_sink);
+    const bool full = block_full<kBR, kBC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
     const float alpha = softmax_step<NT>(sacc, full, i, k0, h, p, m2, l);
 
 #pragma unroll
@@ -583,15 +488,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
           *reinterpret_cast<f32x4*>(Oh + d) = w;
         }
       }
-    if (h == 0) p.lse[(size_t)bh * S + i] = (m2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (h == 0) p.lse[(size_t)bh * S + i] = (m2 + fast_log2(l_tot)) * kLn2;
   }
 }
 
 // ------------------------------------------------------------------------ //
 // Host-side launch.
 // ------------------------------------------------------------------------ //
-int tile_rows() { return kBR; }
-int tile_keys() { return kBC; }
+int generic_tile_rows() { return kBR; }
+int generic_tile_keys() { return kBC; }
 
 template <typename K>
 static hipError_t launch_kernel(K kernel, const FwdParams& p, unsigned grid, hipStream_t st) {
@@ -620,7 +525,7 @@ static hipError_t launch_f32(const FwdParams& p, int D, unsigned grid, hipStream
   }
 }
 
-hipError_t launch_fwd(const FwdParams& p, int D, int dtype, hipStream_t st) {
+hipError_t launch_generic(const FwdParams& p, int D, int dtype, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH;
   switch (dtype) {
     case kDtypeBF16: return launch_half<__bf16>(p, D, grid, st);

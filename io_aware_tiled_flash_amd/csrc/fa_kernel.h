@@ -20,7 +20,7 @@ struct FwdParams {
   unsigned long long* block_pairs;  // optional instrumentation counter (may be null)
   int S;        // sequence length
   int BH;       // batch * heads
-  int nqb;      // query blocks per head = ceil(S / tile_rows())
+  int nqb;      // query blocks per head = ceil(S / block_q of the chosen kernel)
   int causal;   // 0 / 1
   int window;   // 0 = none
   int n_sink;   // leading always-visible keys (only with window > 0)
@@ -28,10 +28,24 @@ struct FwdParams {
   int neg;      // scale < 0
 };
 
-int tile_rows();   // query rows per work-group
-int tile_keys();   // keys per streamed block
+// Generic kernels: every dtype, D in {16, 32, 64, 128}.
+int generic_tile_rows();
+int generic_tile_keys();
+hipError_t launch_generic(const FwdParams& p, int D, int dtype, hipStream_t st);
 
-// Enqueues the kernel for (D, dtype) on `st`; returns the launch status.
-hipError_t launch_fwd(const FwdParams& p, int D, int dtype, hipStream_t st);
+// Fast kernels: bf16 / f16 with D in {64, 128}; nw = waves per work-group (4 or 8).
+bool fast_supported(int D, int dtype);
+int fast_tile_keys();
+hipError_t launch_fast(const FwdParams& p, int D, int dtype, int nw, hipStream_t st);
+
+// Which kernel and tile a problem runs with (host-only, pure function of the shape).
+struct Plan {
+  bool fast;
+  int nw;        // waves per work-group of the fast kernel
+  int block_q;   // query rows per work-group
+  int block_k;   // keys per streamed block
+};
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype);
+hipError_t launch_plan(const Plan& plan, const FwdParams& p, int D, int dtype, hipStream_t st);
 
 }  // namespace fa

@@ -53,12 +53,12 @@ def test_version_and_tile_shape():
     assert "gfx950" in fa.flash_attn_version()
     for D in (16, 32, 64, 128):
         for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
-            bq, bk = fa.flash_attn_tile_shape(D, dt)
+            bq, bk = fa.flash_attn_tile_shape(1, 1, 4096, D, dt)
             assert bq >= 32 and bk >= 32 and bq % 32 == 0 and bk % 32 == 0
     with pytest.raises(NotImplementedError):
-        fa.flash_attn_tile_shape(48, fa.FA_BF16)
+        fa.flash_attn_tile_shape(1, 1, 64, 48, fa.FA_BF16)
     with pytest.raises(ValueError):
-        fa.flash_attn_tile_shape(64, 7)
+        fa.flash_attn_tile_shape(1, 1, 64, 64, 7)
 
 
 def _call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, S=64, D=64, causal=0, window=0, n_sink=0,
@@ -127,7 +127,7 @@ def test_index_range_limit():
 def test_error_text_clears_on_success_path_queries():
     _call(q=None)
     assert fa.flash_attn_last_error()
-    fa.flash_attn_tile_shape(64, fa.FA_F16)
+    fa.flash_attn_tile_shape(1, 1, 64, 64, fa.FA_F16)
     assert fa.flash_attn_last_error() == ""
 
 

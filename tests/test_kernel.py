@@ -235,7 +235,7 @@ def _pairs_with_visible_keys(S, bq, bk, causal, window, n_sink):
     (8192, True, 1024, 4), (3000, True, 200, 70), (3000, True, 200, 0)])
 def test_block_pairs_visited(S, causal, window, n_sink):
     D = 128
-    bq, bk = fa.flash_attn_tile_shape(D, fa.FA_BF16)
+    bq, bk = fa.flash_attn_tile_shape(1, 1, S, D, fa.FA_BF16)
     q, k, v = fa_inputs.make_qkv(1, 1, S, D, "bf16", seed=1)
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     qd, kd, vd = (t.cuda() for t in (q, k, v))
