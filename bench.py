@@ -11,8 +11,10 @@ the work; the kept-pair count is reported beside it in `config`).
 `roofline` describes the forward kernel: achieved = algorithmic FLOPs of one
 launch / mean launch duration (HIP events on the stream the kernel runs on);
 peak = MI355X dense bf16/fp16 MFMA (2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096
-FLOP/clk) or fp32 MFMA (157.3 TFLOP/s). `cpu_baseline` times the fp64 CPU
-oracle on a bounded sample of the same workload (a few heads, all rows).
+FLOP/clk) or fp32 MFMA (157.3 TFLOP/s); traffic = counter-measured HBM bytes
+per launch when the kernel sources match those the counters were taken on,
+else null. `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
+same workload (whole heads, all rows, sized to ~20 s).
 """
 from __future__ import annotations
 
@@ -29,6 +31,28 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the forward kernel, measured with rocprofv3 counter runs
+# (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors a 256 MiB device copy
+# of known size gives), keyed by workload and the SHA-256 of the kernel sources
+# the counters were taken on. Any other source tree reports traffic = null.
+KERNEL_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_fwd_fast.hip",
+                  "io_aware_tiled_flash_amd/csrc/fa_device.h",
+                  "io_aware_tiled_flash_amd/csrc/fa_kernel.h"]
+MEASURED_TRAFFIC = {
+    ("causal_b4h16s4096d128_bf16",
+     "7b5ecdae0417b67f2e04ba55d435343d5390bcb3e6d11bb43324f2bd1befd312"):
+        2.0 * 222431.9 * 1024 + 1.0 * 66560.8 * 1024,
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -47,11 +71,15 @@ def parse():
 
 
 def copy_probe(mib: int, steps: int):
+    """Device-to-device copies of `mib` MiB, each preceded by writing a 1 GiB
+    buffer so that the source is no longer held in L2 / Infinity Cache."""
     import torch
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    flush = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
     for _ in range(steps):
+        flush.fill_(1.0)
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read_per_launch": n * 4,
@@ -82,8 +110,10 @@ def kept_pairs(w) -> int:
     return tot
 
 
-def cpu_baseline(w, q, k, v, n_heads: int):
-    """Time the fp64 oracle on the first n_heads (b, h) heads, all rows."""
+def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
+    """Time the fp64 oracle on the first n_heads (b, h) heads, all rows. With
+    n_heads = 0 the sample is sized from one timed head to about budget_s seconds
+    (capped at the whole workload)."""
     import numpy as np
     from oracle import attention as oracle
     import fa_inputs
@@ -92,14 +122,25 @@ def cpu_baseline(w, q, k, v, n_heads: int):
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)][:n_heads]
-    arrs = [(fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, h:h + 1]),
-             fa_inputs.to_f64(v[b:b + 1, h:h + 1])) for b, h in heads]
-    t0 = time.perf_counter()
-    for qq, kk, vv in arrs:
-        oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale, window=w.window,
-                             n_sink=w.n_sink)
-    dt = time.perf_counter() - t0
+    all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def head(b, h):
+        return (fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, h:h + 1]),
+                fa_inputs.to_f64(v[b:b + 1, h:h + 1]))
+
+    def run(arrs):
+        t0 = time.perf_counter()
+        for qq, kk, vv in arrs:
+            oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale, window=w.window,
+                                 n_sink=w.n_sink)
+        return time.perf_counter() - t0
+
+    if n_heads <= 0:
+        run([head(*all_heads[0])])                  # first call warms the BLAS threads
+        t_one = run([head(*all_heads[0])])
+        n_heads = max(1, min(len(all_heads), int(budget_s / max(t_one, 1e-3))))
+    heads = all_heads[:n_heads]
+    dt = run([head(b, h) for b, h in heads])
     flops = nominal_flops(w) * len(heads) / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(heads)} of {w.B * w.H} heads (all {w.S} rows each) of the same "
@@ -186,15 +227,15 @@ def main():
                    "alg_hbm_bytes_per_step": alg_bytes,
                    "alg_hbm_GBps": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": MEASURED_TRAFFIC.get((name, kernel_source_hash())),  # bytes per launch
                      "kernel": kernel_name(fa, w),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_heads or max(1, min(w.B * w.H, int(2 ** 26 // (w.S * w.S) * 8)))
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, n)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_sample_heads)
     print(json.dumps(out), flush=True)
 
 

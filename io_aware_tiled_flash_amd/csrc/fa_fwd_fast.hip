@@ -4,12 +4,12 @@
 // Same algorithm as the generic kernels (Lab 3 page "Tiled attention with
 // online softmax"; Lesson 91 deck, slide 11): a query block streams over
 // key/value blocks under the online-softmax rescale and writes O / l and the
-// logsumexp once. What differs is how the tiles reach the matrix cores:
+// logsumexp once. What differs is how the work is fed to the matrix cores:
 //
 //  * K and V tiles go HBM -> LDS with direct-to-LDS loads
 //    (global_load_lds_dwordx4): no staging registers, no VALU. Each wave
 //    fills a contiguous 1 KiB run of LDS per instruction, so the XOR
-//    swizzle of the LDS layout is applied on the global-address side.
+//    swizzles of the LDS layouts are applied on the global-address side.
 //  * K is stored row-major with its 16-byte chunks XOR-swizzled by row, so
 //    the 32 lanes reading one chunk column of 32 keys (the A operand of
 //    S^T = K Q^T on v_mfma_f32_32x32x16) hit distinct LDS banks.
@@ -25,16 +25,16 @@
 //  * Lazy rescale: a row's running max only moves (and O, l are only
 //    rescaled) when the new block max exceeds it by more than 2^8 in the
 //    base-2 exponent; otherwise the stale max is kept and exp2 arguments stay
-//    <= 8. The result O / l is unchanged by the choice of reference max, and
-//    fp32 holds the <= 256x larger partial sums without loss. The decision is
-//    wave-uniform, so the 64-multiply rescale of O is skipped as a branch.
+//    <= 8. The result O / l does not depend on the reference max, and fp32
+//    holds the <= 256x larger partial sums without loss. The decision is
+//    wave-uniform, so the rescale of O is skipped as a branch.
 //  * Masks are applied only to partially visible blocks, with per-lane
 //    bounds and compile-time key offsets (two VALU ops per score).
-//  * K/V are double-buffered: block it+1 is in flight into the other buffer
-//    while block it is computed; one barrier per block.
-
+//
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_kernel.h"
@@ -43,14 +43,14 @@ namespace fa {
 
 namespace {
 
-constexpr int kBCf = 64;   // keys per streamed block
+constexpr int kBCf = 64;     // keys per streamed block
 constexpr float kTau = 8.f;  // lazy-rescale threshold (base-2 exponent)
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS element offset of K[row][chunk*8] (16-byte chunks swizzled by row).
+// 16-byte chunk swizzle of the K layout.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -66,11 +66,17 @@ __device__ __forceinline__ int v_swz(int row) {
 // (row, physical chunk) = divmod(pos, D/8) and receives the logical chunk the
 // swizzle maps there. Rows past the sequence end re-read row S-1 (finite
 // data; every such key is masked out).
+template <int D, int NW>
+struct TileLoad {
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int NI = kBCf * CPR / (64 * NW);    // instructions per wave per tile
+};
+
 template <int D, int NW, bool IS_V, typename T>
 __device__ __forceinline__ void tile_to_lds(T* lds_tile, const T* __restrict__ g, int k0, int S,
                                             int wave, int lane) {
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int NI = kBCf * CPR / (64 * NW);    // instructions per wave
+  constexpr int CPR = TileLoad<D, NW>::CPR;
+  constexpr int NI = TileLoad<D, NW>::NI;
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int base = (wave * NI + n) * 64;
@@ -91,9 +97,12 @@ __device__ __forceinline__ void tile_to_lds(T* lds_tile, const T* __restrict__ g
   }
 }
 
-__device__ __forceinline__ void wait_vmem_all() {
-  // s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
 template <typename T>
@@ -102,143 +111,110 @@ __device__ __forceinline__ u32x2 lds_tr_read(const T* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-}  // namespace
-
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_fast_kernel(FwdParams p) {
+// Per-lane state and block operations shared by both schedules. One wave
+// owns 32 query rows; lane (col, h) = (lane & 31, lane >> 5) owns query row
+// i = q_lo + 32 * wave_in_block + col and, in every 32-key sub-tile, the keys
+// 8 g + 4 h + r (g, r < 4) of the S^T accumulator.
+template <typename T, int D, int BR>
+struct Core {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
-  constexpr int BR = 32 * NW;
-  constexpr int BC = kBCf;
-  constexpr int NT = BC / 32;     // 32-key sub-tiles
-  constexpr int NDT = D / 32;     // 32-wide d tiles of O^T
-  constexpr int NS = D / 16;      // k-steps of QK^T
-  constexpr int TILE = BC * D;    // elements per K or V tile
+  static constexpr int BC = kBCf;
+  static constexpr int NT = BC / 32;   // 32-key sub-tiles
+  static constexpr int NDT = D / 32;   // 32-wide d tiles of O^T
+  static constexpr int NS = D / 16;    // k-steps of QK^T
 
-  __shared__ __attribute__((aligned(1024))) T lds[2][2][TILE];   // [buffer][K, V]
+  v8 qf[NS];         // Q fragment (B operand of S^T = K Q^T)
+  int koff[NS];      // LDS offsets of the K fragment per k-step
+  int vdt[NDT];      // LDS offsets of the V^T fragment reads per d tile
+  f32x16 oacc[NDT];  // O^T accumulator
+  float m_run;       // running max (raw sign-folded score units)
+  float mc;          // m_run * c, or 0 while nothing is visible
+  float l;           // this lane half's running sum
+  float c, tau_raw;
+  int i, h, col;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int col = lane & 31;
-
-  int qb, bh;
-  wg_coords(p, qb, bh);
-  const int S = p.S;
-  const int q_lo = qb * BR;
-  const int i = q_lo + 32 * wave + col;   // this lane's query row
-  const size_t head = (size_t)bh * (size_t)S * D;
-  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + head;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + head;
-
-  const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
-  const int n_iter = br.count();
-  if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
-
-  // Block 0 in flight while Q is fetched.
-  tile_to_lds<D, NW, false>(&lds[0][0][0], Kh, br.kb(0) * BC, S, wave, lane);
-  tile_to_lds<D, NW, true>(&lds[0][1][0], Vh, br.kb(0) * BC, S, wave, lane);
-
-  // Q fragment (B operand of S^T = K Q^T): lane holds Q[i][16 s + 8 h .. +7].
-  v8 qf[NS];
+  __device__ __forceinline__ void init(const FwdParams& p, const T* __restrict__ Qh, int q_row,
+                                       int lane) {
+    h = lane >> 5;
+    col = lane & 31;
+    i = q_row;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (i < S) w = *reinterpret_cast<const u32x4*>(Qh + (size_t)i * D + 16 * s + 8 * h);
-    if (p.neg) w ^= 0x80008000u;
-    qf[s] = __builtin_bit_cast(v8, w);
-  }
-
-  // Per-lane LDS offsets (elements) of the K fragment (A of S^T) for each
-  // k-step s, relative to the 32-key sub-tile base.
-  int koff[NS];
-  {
+    for (int s = 0; s < NS; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (i < p.S) w = *reinterpret_cast<const u32x4*>(Qh + (size_t)i * D + 16 * s + 8 * h);
+      if (p.neg) w ^= 0x80008000u;
+      qf[s] = __builtin_bit_cast(v8, w);
+    }
     const int sw = k_swz<D>(col);
 #pragma unroll
     for (int s = 0; s < NS; ++s) koff[s] = col * D + (((2 * s + h) ^ sw) << 3);
+    const int r16 = lane & 15;
+    const int grp = (lane >> 4) & 1;
+    const int vsw = D == 128 ? ((r16 >> 2) & 3) : ((r16 >> 3) & 1);
+    const int vbase = (4 * h + (r16 >> 2)) * D + 16 * grp + 4 * (r16 & 3);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vdt[dt] = vbase + ((dt ^ vsw) << 5);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    m_run = kNegInf;
+    mc = 0.f;
+    l = 0.f;
+    c = p.c;
+    tau_raw = kTau / c;
   }
-  // Per-lane LDS offsets of the V^T fragment (A of O^T) transposed reads.
-  const int r16 = lane & 15;
-  const int grp = (lane >> 4) & 1;
-  const int vsw = D == 128 ? ((r16 >> 2) & 3) : ((r16 >> 3) & 1);
-  const int vbase = (4 * h + (r16 >> 2)) * D + 16 * grp + 4 * (r16 & 3);
-  int vdt[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) vdt[dt] = vbase + ((dt ^ vsw) << 5);
 
-  f32x16 oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = kNegInf;   // running max (raw sign-folded score units)
-  float mc = 0.f;          // m_run * c, or 0 while nothing is visible
-  float l = 0.f;           // this lane half's running sum
-  const float c = p.c;
-  const float tau_raw = kTau / c;
-
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const int k0 = br.kb(it) * BC;
-    if (it + 1 < n_iter) {
-      const int k1 = br.kb(it + 1) * BC;
-      tile_to_lds<D, NW, false>(&lds[buf ^ 1][0][0], Kh, k1, S, wave, lane);
-      tile_to_lds<D, NW, true>(&lds[buf ^ 1][1][0], Vh, k1, S, wave, lane);
-    }
-    const T* Ks = &lds[buf][0][0];
-    const T* Vs = &lds[buf][1][0];
-
-    // S^T = K Q^T
-    f32x16 sacc[NT];
+  // S^T = K Q^T for the K tile at ks.
+  __device__ __forceinline__ void qk(f32x16 (&acc)[NT], const T* ks) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        v8 a = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(Ks + 32 * t * D + koff[s]));
-        sacc[t] = Tr::mma(a, qf[s], sacc[t]);
+        v8 a = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(ks + 32 * t * D + koff[s]));
+        acc[t] = Tr::mma(a, qf[s], acc[t]);
       }
     }
+  }
 
-    // Mask partially visible blocks: key j = k0 + 4h + e, e = 32t + 8g + r.
-    if (!block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink)) {
-      const int jb = k0 + 4 * h;
-      const int hi = (p.causal ? min(i, S - 1) : S - 1) - jb;
-      if (p.window > 0) {
-        const int lo = i - p.window + 1 - jb;
-        const int sk = p.n_sink - 1 - jb;
+  // Mask the scores of a partially visible block: key j = k0 + 4h + e,
+  // e = 32t + 8g + r.
+  __device__ __forceinline__ void mask(f32x16 (&acc)[NT], const FwdParams& p, int k0) const {
+    const int jb = k0 + 4 * h;
+    const int hi = (p.causal ? min(i, p.S - 1) : p.S - 1) - jb;
+    if (p.window > 0) {
+      const int lo = i - p.window + 1 - jb;
+      const int sk = p.n_sink - 1 - jb;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = 32 * t + 8 * (r >> 2) + (r & 3);
-            const bool keep = (e <= hi) & ((e >= lo) | (e <= sk));
-            sacc[t][r] = keep ? sacc[t][r] : kNegInf;
-          }
-      } else {
+        for (int r = 0; r < 16; ++r) {
+          const int e = 32 * t + 8 * (r >> 2) + (r & 3);
+          const bool keep = (e <= hi) & ((e >= lo) | (e <= sk));
+          acc[t][r] = keep ? acc[t][r] : kNegInf;
+        }
+    } else {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int e = 32 * t + 8 * (r >> 2) + (r & 3);
-            sacc[t][r] = (e <= hi) ? sacc[t][r] : kNegInf;
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int e = 32 * t + 8 * (r >> 2) + (r & 3);
+          acc[t][r] = (e <= hi) ? acc[t][r] : kNegInf;
+        }
     }
+  }
 
-    // Online softmax with lazy rescale.
-    float mt = sacc[0][0];
+  // Online softmax with lazy rescale: turns the (masked) scores into p,
+  // adds them to l and packs them into the B operands of the PV MFMA.
+  __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2]) {
+    float mt = acc[0][0];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mt = fmaxf(mt, sacc[t][r]);
+      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mt = fmaxf(mt, acc[t][r]);
     mt = xhalf_max(mt);
     const float m_new = fmaxf(m_run, mt);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + tau_raw)) {
@@ -252,32 +228,33 @@ void fa_fwd_fast_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
-    v8 pb[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(sacc[t][r], c, -mc));
-        sacc[t][r] = e;
+        const float e = fast_exp2(__builtin_fmaf(acc[t][r], c, -mc));
+        acc[t][r] = e;
         l += e;
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         u32x4 w;
-        w[0] = pack2<T>(sacc[t][8 * u + 0], sacc[t][8 * u + 1]);
-        w[1] = pack2<T>(sacc[t][8 * u + 2], sacc[t][8 * u + 3]);
-        w[2] = pack2<T>(sacc[t][8 * u + 4], sacc[t][8 * u + 5]);
-        w[3] = pack2<T>(sacc[t][8 * u + 6], sacc[t][8 * u + 7]);
+        w[0] = pack2<T>(acc[t][8 * u + 0], acc[t][8 * u + 1]);
+        w[1] = pack2<T>(acc[t][8 * u + 2], acc[t][8 * u + 3]);
+        w[2] = pack2<T>(acc[t][8 * u + 4], acc[t][8 * u + 5]);
+        w[3] = pack2<T>(acc[t][8 * u + 6], acc[t][8 * u + 7]);
         pb[t][u] = __builtin_bit_cast(v8, w);
       }
     }
+  }
 
-    // O^T += V^T P^T; the V^T fragment comes from two transposed LDS reads.
+  // O^T += V^T P^T for the V tile at vs (two transposed reads per operand).
+  __device__ __forceinline__ void pv(const T* vs, const v8 (&pb)[NT][2]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const T* vk = Vs + (32 * t + 16 * u) * D;
+        const T* vk = vs + (32 * t + 16 * u) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const u32x2 lo = lds_tr_read(vk + vdt[dt]);
@@ -286,28 +263,109 @@ void fa_fwd_fast_kernel(FwdParams p) {
           oacc[dt] = Tr::mma(__builtin_bit_cast(v8, w), pb[t][u], oacc[dt]);
         }
       }
+  }
 
-    wait_vmem_all();
+  // O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
+  __device__ __forceinline__ void epilogue(const FwdParams& p, size_t head, int bh) {
+    const float l_tot = xhalf_sum(l);
+    if (i < p.S) {
+      const float inv = 1.f / l_tot;
+      T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head + (size_t)i * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * h;
+          u32x2 w;
+          w[0] = pack2<T>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
+          w[1] = pack2<T>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(Oh + d) = w;
+        }
+      if (h == 0) p.lse[(size_t)bh * p.S + i] = (mc + fast_log2(l_tot)) * kLn2;
+    }
+  }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------------ //
+// The kernel. Every wave runs QK^T, mask, softmax and PV for block j while
+// the direct-to-LDS loads of block j+1 land in the other K/V buffer pair; one
+// barrier per block. The two buffer pairs are distinct __shared__ objects and
+// the block loop is unrolled by two, so every LDS access names its buffer at
+// compile time: the compiler can then tell the DMA target from the buffer
+// being read and does not wait for the in-flight loads before each read (it
+// would have to if both were slots of one array picked at run time).
+// ------------------------------------------------------------------------ //
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_fast_kernel(FwdParams p) {
+  constexpr int BR = 32 * NW;
+  constexpr int BC = kBCf;
+  using C = Core<T, D, BR>;
+  constexpr int TILE = BC * D;
+
+  __shared__ __attribute__((aligned(1024))) T k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v1s[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  int qb, bh;
+  wg_coords(p, qb, bh);
+  const int S = p.S;
+  const int q_lo = qb * BR;
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + head;
+
+  const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
+  const int n_iter = br.count();
+  if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
+
+  // Block 0 in flight while Q is fetched.
+  tile_to_lds<D, NW, false>(k0s, Kh, br.kb(0) * BC, S, wave, lane);
+  tile_to_lds<D, NW, true>(v0s, Vh, br.kb(0) * BC, S, wave, lane);
+
+  C core;
+  core.init(p, Qh, q_lo + 32 * wave + (lane & 31), lane);
+
+  wait_vmem<0>();
+  __syncthreads();
+
+  // Block `it` computed from buffer pair PAR while block it+1 loads into the other.
+  auto step = [&](auto par, int it) {
+    constexpr int PAR = decltype(par)::value;
+    T* kc = PAR == 0 ? k0s : k1s;
+    T* vc = PAR == 0 ? v0s : v1s;
+    T* kn = PAR == 0 ? k1s : k0s;
+    T* vn = PAR == 0 ? v1s : v0s;
+    const int k0 = br.kb(it) * BC;
+    if (it + 1 < n_iter) {
+      const int k1 = br.kb(it + 1) * BC;
+      tile_to_lds<D, NW, false>(kn, Kh, k1, S, wave, lane);
+      tile_to_lds<D, NW, true>(vn, Vh, k1, S, wave, lane);
+    }
+    f32x16 sacc[C::NT];
+    core.qk(sacc, kc);
+    if (!block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink)) core.mask(sacc, p, k0);
+    typename C::v8 pb[C::NT][2];
+    core.softmax(sacc, pb);
+    core.pv(vc, pb);
+    wait_vmem<0>();
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 2 <= n_iter; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
-
-  // Epilogue: O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
-  const float l_tot = xhalf_sum(l);
-  if (i < S) {
-    const float inv = 1.f / l_tot;
-    T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head + (size_t)i * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * h;
-        u32x2 w;
-        w[0] = pack2<T>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-        w[1] = pack2<T>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(Oh + d) = w;
-      }
-    if (h == 0) p.lse[(size_t)bh * S + i] = (mc + fast_log2(l_tot)) * kLn2;
-  }
+  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
+  core.epilogue(p, head, bh);
 }
 
 // ------------------------------------------------------------------------ //
