@@ -5,8 +5,9 @@
 One step = one forward pass (both contractions, online softmax, epilogue) over
 the whole batch of the workload, inputs already resident in HBM. Prints ONE
 JSON line. Throughput is TFLOP/s with FLOPs = 4*B*H*S^2*D, halved under the
-causal mask (for the window+sink workload the nominal causal figure overstates
-the work; the kept-pair count is reported beside it in `config`).
+causal mask; under a sliding window (+ sinks) FLOPs = 4*B*H*D*(kept query-key
+pairs), since the nominal causal figure would count the keys the window drops
+(it is reported beside it in `config`).
 
 `roofline` describes the forward kernel: achieved = algorithmic FLOPs of one
 launch / mean launch duration (HIP events on the stream the kernel runs on);
@@ -95,8 +96,18 @@ def kernel_name(fa, w) -> str:
 
 
 def nominal_flops(w) -> float:
+    """4*B*H*S^2*D, halved under the causal mask."""
     f = 4.0 * w.B * w.H * w.S * w.S * w.D
     return f / 2.0 if w.causal else f
+
+
+def algorithmic_flops(w) -> float:
+    """FLOPs of the two contractions over the (query, key) pairs the mask keeps.
+    Equal to the nominal figure up to the causal diagonal; under a sliding window
+    the nominal causal figure would count keys the window drops."""
+    if w.causal and 0 < w.window < w.S:
+        return 4.0 * w.B * w.H * w.D * kept_pairs(w)
+    return nominal_flops(w)
 
 
 def kept_pairs(w) -> int:
@@ -141,7 +152,7 @@ def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
         n_heads = max(1, min(len(all_heads), int(budget_s / max(t_one, 1e-3))))
     heads = all_heads[:n_heads]
     dt = run([head(b, h) for b, h in heads])
-    flops = nominal_flops(w) * len(heads) / (w.B * w.H)
+    flops = algorithmic_flops(w) * len(heads) / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(heads)} of {w.B * w.H} heads (all {w.S} rows each) of the same "
                       f"workload, fp64 NumPy, {dt:.2f} s wall"}
@@ -198,7 +209,7 @@ def main():
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
 
-    flops = nominal_flops(w)
+    flops = algorithmic_flops(w)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
@@ -222,7 +233,8 @@ def main():
         "config": {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": w.window, "n_sink": w.n_sink,
                    "scale": w.scale, "layout": "[B,H,S,D] contiguous",
-                   "flops_per_step": flops, "kept_pairs_per_head": kept_pairs(w),
+                   "flops_per_step": flops, "nominal_flops_per_step": nominal_flops(w),
+                   "kept_pairs_per_head": kept_pairs(w),
                    "frac_of_peak_wall": round(value / peak, 4),
                    "alg_hbm_bytes_per_step": alg_bytes,
                    "alg_hbm_GBps": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1)},
