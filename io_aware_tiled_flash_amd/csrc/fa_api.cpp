@@ -116,16 +116,19 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
 
 namespace fa {
 
-// Kernel choice. bf16/f16 with D = 64 or 128 take the fast kernel; its
-// work-group holds 8 waves (256 query rows share each K/V tile) when that
-// still yields at least two work-groups per CU (256 CUs), else 4 waves.
-// FLASH_ATTN_WAVES=4|8 overrides the wave count (tuning only).
+// Kernel choice. bf16/f16 with D = 64 or 128 take the fast kernel. Its
+// work-group holds 4 waves (128 query rows), so two work-groups share a CU and
+// run out of step with each other: one's softmax (vector ALU) overlaps the
+// other's matrix products. Only for very long sequences (S >= 16384, with at
+// least two 8-wave work-groups per CU) do 8 waves win, by halving the K/V
+// tile traffic per query row. FLASH_ATTN_WAVES=4|8 overrides the wave count
+// (tuning only).
 Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype) {
   Plan pl;
   if (fast_supported((int)D, dtype)) {
     pl.fast = true;
     const int64_t wgs8 = BH * ((S + 255) / 256);
-    pl.nw = wgs8 >= 512 ? 8 : 4;
+    pl.nw = (S >= 16384 && wgs8 >= 512) ? 8 : 4;
     if (const char* e = std::getenv("FLASH_ATTN_WAVES")) {
       const int v = std::atoi(e);
       if (v == 4 || v == 8) pl.nw = v;

@@ -6,10 +6,13 @@
 // key/value blocks under the online-softmax rescale and writes O / l and the
 // logsumexp once. What differs is how the work is fed to the matrix cores:
 //
-//  * K and V tiles go HBM -> LDS with direct-to-LDS loads
-//    (global_load_lds_dwordx4): no staging registers, no VALU. Each wave
-//    fills a contiguous 1 KiB run of LDS per instruction, so the XOR
-//    swizzles of the LDS layouts are applied on the global-address side.
+//  * K and V tiles go HBM -> LDS with direct-to-LDS buffer loads
+//    (buffer_load_dwordx4 ... lds): no staging registers and, since the
+//    per-lane offsets are fixed and the block's position lives in the scalar
+//    buffer descriptor, no per-block address arithmetic. The descriptor's
+//    size ends at the sequence end, so a ragged last block reads zeros past
+//    it. Each wave fills a contiguous 1 KiB run of LDS per instruction, so
+//    the XOR swizzles of the LDS layouts are applied on the global side.
 //  * K is stored row-major with its 16-byte chunks XOR-swizzled by row, so
 //    the 32 lanes reading one chunk column of 32 keys (the A operand of
 //    S^T = K Q^T on v_mfma_f32_32x32x16) hit distinct LDS banks.
@@ -29,7 +32,10 @@
 //    holds the <= 256x larger partial sums without loss. The decision is
 //    wave-uniform, so the rescale of O is skipped as a branch.
 //  * Masks are applied only to partially visible blocks, with per-lane
-//    bounds and compile-time key offsets (two VALU ops per score).
+//    bounds and compile-time key offsets (two VALU ops per score). The
+//    partially visible blocks sit at the two ends of the visiting order, so
+//    the loop runs in three segments and only the end segments carry mask
+//    code.
 //
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -45,6 +51,9 @@ namespace {
 
 constexpr int kBCf = 64;     // keys per streamed block
 constexpr float kTau = 8.f;  // lazy-rescale threshold (base-2 exponent)
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format,
+// no swizzle, no stride): offsets at or past the size read as zero.
+constexpr int kBufferFlags = 0x00020000;
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -61,41 +70,54 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? (row & 3) : ((row >> 1) & 1);
 }
 
-// Direct HBM -> LDS copy of one BC x D tile (K if IS_V is false, else V).
-// Wave w fills LDS 16-byte positions [w*NI*64, (w+1)*NI*64); position pos is
-// (row, physical chunk) = divmod(pos, D/8) and receives the logical chunk the
-// swizzle maps there. Rows past the sequence end re-read row S-1 (finite
-// data; every such key is masked out).
-template <int D, int NW>
-struct TileLoad {
+// Direct HBM -> LDS copy of one BC x D tile (K if IS_V is false, else V)
+// with buffer loads: wave w fills LDS 16-byte positions [w*NI*64,
+// (w+1)*NI*64); position pos is (row, physical chunk) = divmod(pos, D/8) and
+// receives the logical chunk the swizzle maps there. The per-lane byte
+// offsets are fixed for the whole kernel; the buffer descriptor is rebuilt per
+// block with its base at the block's first key and its size ending at the
+// sequence end, so rows past the end read as zeros (every such key is masked
+// out).
+template <typename T, int D, int NW, bool IS_V>
+struct TileDma {
   static constexpr int CPR = D / 8;                    // 16-byte chunks per row
   static constexpr int NI = kBCf * CPR / (64 * NW);    // instructions per wave per tile
-};
+  static_assert(NI >= 1 && NI * 64 * NW == kBCf * CPR, "tile / wave split");
+  uint32_t voff[NI];
 
-template <int D, int NW, bool IS_V, typename T>
-__device__ __forceinline__ void tile_to_lds(T* lds_tile, const T* __restrict__ g, int k0, int S,
-                                            int wave, int lane) {
-  constexpr int CPR = TileLoad<D, NW>::CPR;
-  constexpr int NI = TileLoad<D, NW>::NI;
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int base = (wave * NI + n) * 64;
-    const int pos = base + lane;
-    const int row = pos / CPR;
-    const int pc = pos % CPR;
-    int d;
-    if (IS_V) {
-      const int seg = (pc >> 2) ^ v_swz<D>(row);
-      d = 32 * seg + 8 * (pc & 3);
-    } else {
-      d = 8 * (pc ^ k_swz<D>(row));
+    for (int n = 0; n < NI; ++n) {
+      const int pos = (wave * NI + n) * 64 + lane;
+      const int row = pos / CPR;
+      const int pc = pos % CPR;
+      int d;
+      if (IS_V) {
+        const int seg = (pc >> 2) ^ v_swz<D>(row);
+        d = 32 * seg + 8 * (pc & 3);
+      } else {
+        d = 8 * (pc ^ k_swz<D>(row));
+      }
+      voff[n] = (uint32_t)((row * D + d) * (int)sizeof(T));
     }
-    const int grow = min(k0 + row, S - 1);
-    const T* src = g + (size_t)grow * D + d;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                     (lds_void*)(lds_tile + base * 8), 16, 0, 0);
   }
-}
+
+  __device__ __forceinline__ void load(T* lds_tile, const T* __restrict__ g, int k0, int S,
+                                       int wave) const {
+    // Base and size are wave-uniform; readfirstlane keeps them in scalar
+    // registers, where the descriptor must live.
+    const uint64_t base = reinterpret_cast<uint64_t>(g + (size_t)k0 * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane((S - k0) * D * (int)sizeof(T));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * NI + n) * 512),
+                                               16, voff[n], 0, 0, 0);
+  }
+};
 
 // s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]).
@@ -130,7 +152,7 @@ struct Core {
   f32x16 oacc[NDT];  // O^T accumulator
   float m_run;       // running max (raw sign-folded score units)
   float mc;          // m_run * c, or 0 while nothing is visible
-  float l;           // this lane half's running sum
+  float l[4];        // this lane half's running sum, in 4 parts
   float c, tau_raw;
   int i, h, col;
 
@@ -161,7 +183,8 @@ struct Core {
       for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
     m_run = kNegInf;
     mc = 0.f;
-    l = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l[k] = 0.f;
     c = p.c;
     tau_raw = kTau / c;
   }
@@ -222,7 +245,8 @@ struct Core {
       const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
       m_run = m_new;
       mc = mc_new;
-      l *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) l[k] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -234,7 +258,7 @@ struct Core {
       for (int r = 0; r < 16; ++r) {
         const float e = fast_exp2(__builtin_fmaf(acc[t][r], c, -mc));
         acc[t][r] = e;
-        l += e;
+        l[r & 3] += e;
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -267,7 +291,7 @@ struct Core {
 
   // O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
   __device__ __forceinline__ void epilogue(const FwdParams& p, size_t head, int bh) {
-    const float l_tot = xhalf_sum(l);
+    const float l_tot = xhalf_sum((l[0] + l[1]) + (l[2] + l[3]));
     if (i < p.S) {
       const float inv = 1.f / l_tot;
       T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head + (size_t)i * D;
@@ -327,9 +351,14 @@ void fa_fwd_fast_kernel(FwdParams p) {
   const int n_iter = br.count();
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
 
+  TileDma<T, D, NW, false> kdma;
+  TileDma<T, D, NW, true> vdma;
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
+
   // Block 0 in flight while Q is fetched.
-  tile_to_lds<D, NW, false>(k0s, Kh, br.kb(0) * BC, S, wave, lane);
-  tile_to_lds<D, NW, true>(v0s, Vh, br.kb(0) * BC, S, wave, lane);
+  kdma.load(k0s, Kh, br.kb(0) * BC, S, wave);
+  vdma.load(v0s, Vh, br.kb(0) * BC, S, wave);
 
   C core;
   core.init(p, Qh, q_lo + 32 * wave + (lane & 31), lane);
@@ -338,33 +367,50 @@ void fa_fwd_fast_kernel(FwdParams p) {
   __syncthreads();
 
   // Block `it` computed from buffer pair PAR while block it+1 loads into the other.
-  auto step = [&](auto par, int it) {
+  // MASK selects the masked variant at compile time: the visiting order is
+  // [partially visible blocks][fully visible blocks][partially visible
+  // blocks] (sinks and the window's first blocks, the interior, the causal
+  // diagonal), and each segment runs its own copy of the loop, so the common
+  // fully visible step carries no mask code and no branch around it.
+  auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     T* kc = PAR == 0 ? k0s : k1s;
     T* vc = PAR == 0 ? v0s : v1s;
     T* kn = PAR == 0 ? k1s : k0s;
     T* vn = PAR == 0 ? v1s : v0s;
-    const int k0 = br.kb(it) * BC;
     if (it + 1 < n_iter) {
       const int k1 = br.kb(it + 1) * BC;
-      tile_to_lds<D, NW, false>(kn, Kh, k1, S, wave, lane);
-      tile_to_lds<D, NW, true>(vn, Vh, k1, S, wave, lane);
+      kdma.load(kn, Kh, k1, S, wave);
+      vdma.load(vn, Vh, k1, S, wave);
     }
     f32x16 sacc[C::NT];
     core.qk(sacc, kc);
-    if (!block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink)) core.mask(sacc, p, k0);
+    if (decltype(mask)::value) core.mask(sacc, p, br.kb(it) * BC);
     typename C::v8 pb[C::NT][2];
     core.softmax(sacc, pb);
     core.pv(vc, pb);
     wait_vmem<0>();
     __syncthreads();
   };
-  int it = 0;
-  for (; it + 2 <= n_iter; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
+  // Steps [b, e) of one segment; the buffer pair alternates with it & 1.
+  auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
+    int it = b;
+    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+    for (; it + 2 <= e; it += 2) {
+      step(std::integral_constant<int, 0>{}, mask, it);
+      step(std::integral_constant<int, 1>{}, mask, it + 1);
+    }
+    if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+  };
+  int f0 = 0;
+  while (f0 < n_iter && !block_full<BR, BC>(q_lo, br.kb(f0) * BC, S, p.causal, p.window, p.n_sink))
+    ++f0;
+  int f1 = f0;
+  while (f1 < n_iter && block_full<BR, BC>(q_lo, br.kb(f1) * BC, S, p.causal, p.window, p.n_sink))
+    ++f1;
+  segment(std::true_type{}, 0, f0);
+  segment(std::false_type{}, f0, f1);
+  segment(std::true_type{}, f1, n_iter);
   core.epilogue(p, head, bh);
 }
 
