@@ -39,6 +39,14 @@ Readings where the pages are silent (each also listed in the design notes):
   R6 LSE_i = m_i + ln(l_i) in the scaled-score domain, natural log.
   R7 a row with no visible key (unreachable under R2: the diagonal is always
      visible) is defined as O = 0, LSE = -inf.
+  R8 grouped K/V heads (Lesson 91 deck, slide 32 "MQA: one shared K, V for all
+     query heads"): with Hq query heads and Hkv key/value heads (Hkv divides
+     Hq), query head h reads key/value head h // (Hq / Hkv), i.e. consecutive
+     query heads form the groups. Hkv = 1 is MQA, Hkv = Hq ordinary attention.
+  R9 ALiBi (Lesson 91 deck, slides 20-25): the logit of (i, j) in head h gains
+     the bias -m_h * |i - j| before the softmax, on top of the scaled score;
+     the slopes are inputs (fp32, rounded first like the scale), and
+     alibi_slopes(H) gives the deck's geometric rule m_h = 2^(-8h/H), h = 1..H.
 
 Every part of this module is pinned by tests against closed forms, brute force,
 invariants and a library routine; see the test module for the oracle.
@@ -73,6 +81,16 @@ def visible(rows: np.ndarray, S: int, causal: bool, window: int = 0,
     return keep
 
 
+def alibi_slopes(H: int) -> np.ndarray:
+    """R9: the deck's slope rule, m_h = 2^(-8h/H) for heads h = 1..H (slide 23)."""
+    return np.array([2.0 ** (-8.0 * h / H) for h in range(1, H + 1)])
+
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """R8: the key/value head that query head h reads."""
+    return h // (Hq // Hkv)
+
+
 def _as_f64(x) -> np.ndarray:
     a = np.asarray(x)
     if a.dtype != np.float64:
@@ -81,13 +99,15 @@ def _as_f64(x) -> np.ndarray:
 
 
 def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
-                  n_sink: int = 0, rows=None, chunk: int = 1024, return_probs: bool = False):
+                  n_sink: int = 0, rows=None, chunk: int = 1024, return_probs: bool = False,
+                  alibi_slopes=None):
     """Materialised attention in fp64.
 
-    q, k, v: arrays [B, H, S, D] (any float dtype; upcast exactly to fp64).
+    q: [B, Hq, S, D]; k, v: [B, Hkv, S, D] with Hkv dividing Hq (R8); any float
+    dtype, upcast exactly to fp64. alibi_slopes: optional [Hq] slopes (R9).
     rows: optional 1-D array of query positions to compute (default: all).
-    Returns (O [B, H, R, D], LSE [B, H, R]) in fp64, R = len(rows); with
-    return_probs=True also the normalised softmax matrix P [B, H, R, S]
+    Returns (O [B, Hq, R, D], LSE [B, Hq, R]) in fp64, R = len(rows); with
+    return_probs=True also the normalised softmax matrix P [B, Hq, R, S]
     (small inputs only).
 
     Each query row's full score row over all S keys is formed at once
@@ -96,10 +116,17 @@ def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, S, D = q.shape
-    if k.shape != (B, H, S, D) or v.shape != (B, H, S, D):
-        raise ValueError("q, k, v must share the shape [B, H, S, D]")
+    Hkv = k.shape[1] if k.ndim == 4 else 0
+    if Hkv < 1 or k.shape != (B, Hkv, S, D) or v.shape != (B, Hkv, S, D) or H % Hkv:
+        raise ValueError("k, v must be [B, Hkv, S, D] with Hkv dividing the query heads")
     s = fp32_scale(scale)
+    slopes = None
+    if alibi_slopes is not None:
+        slopes = np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+        if slopes.shape != (H,):
+            raise ValueError("alibi_slopes must hold one slope per query head")
     rows = np.arange(S, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    j_idx = np.arange(S, dtype=np.int64)[None, :]
     O = np.zeros((B, H, rows.size, D))
     LSE = np.full((B, H, rows.size), _NEG_INF)
     P = np.zeros((B, H, rows.size, S)) if return_probs else None
@@ -107,16 +134,20 @@ def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
         rr = rows[c0:c0 + chunk]
         keep = visible(rr, S, causal, window, n_sink)
         any_visible = keep.any(axis=1)
+        dist = np.abs(rr[:, None] - j_idx).astype(np.float64)
         for b in range(B):
             for h in range(H):
-                scores = (q[b, h, rr, :] @ k[b, h].T) * s          # [rows, S]
+                g = kv_head(h, H, Hkv)
+                scores = (q[b, h, rr, :] @ k[b, g].T) * s          # [rows, S]
+                if slopes is not None:
+                    scores = scores - slopes[h] * dist
                 scores = np.where(keep, scores, _NEG_INF)
                 m = scores.max(axis=1)
                 m_safe = np.where(any_visible, m, 0.0)
                 p = np.exp(scores - m_safe[:, None])                # masked -> 0
                 l = p.sum(axis=1)
                 l_safe = np.where(any_visible, l, 1.0)
-                O[b, h, c0:c0 + rr.size] = (p @ v[b, h]) / l_safe[:, None]
+                O[b, h, c0:c0 + rr.size] = (p @ v[b, g]) / l_safe[:, None]
                 LSE[b, h, c0:c0 + rr.size] = np.where(any_visible, m + np.log(l_safe),
                                                       _NEG_INF)
                 if return_probs:

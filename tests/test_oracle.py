@@ -46,14 +46,19 @@ def _qkv(B, H, S, D, seed):
 # Pins. Each takes the oracle module and raises AssertionError on a mismatch.
 # --------------------------------------------------------------------------- #
 
-def _brute(q, k, v, causal, scale, window, n_sink):
-    """Scalar loops over every (b, h, i, j, d) with math.fsum/exp/log."""
+def _brute(q, k, v, causal, scale, window, n_sink, slopes=None):
+    """Scalar loops over every (b, h, i, j, d) with math.fsum/exp/log. k, v may
+    hold fewer heads (groups of consecutive query heads share one); slopes add
+    the ALiBi term -slope_h |i - j| to each logit."""
     s = float(np.float32(scale))
     B, H, S, D = q.shape
+    G = H // k.shape[1]
     O = np.zeros((B, H, S, D))
     L = np.zeros((B, H, S))
     for b in range(B):
         for h in range(H):
+            hk = h // G
+            m_h = 0.0 if slopes is None else float(np.float32(slopes[h]))
             for i in range(S):
                 keys = []
                 for j in range(S):
@@ -63,12 +68,14 @@ def _brute(q, k, v, causal, scale, window, n_sink):
                         if window > 0 and i - j >= window and j >= n_sink:
                             continue
                     keys.append(j)
-                sc = [s * math.fsum(q[b, h, i, d] * k[b, h, j, d] for d in range(D)) for j in keys]
+                sc = [s * math.fsum(q[b, h, i, d] * k[b, hk, j, d] for d in range(D))
+                      - m_h * abs(i - j) for j in keys]
                 mx = max(sc)
                 e = [math.exp(x - mx) for x in sc]
                 tot = math.fsum(e)
                 for d in range(D):
-                    O[b, h, i, d] = math.fsum(e[t] * v[b, h, j, d] for t, j in enumerate(keys)) / tot
+                    O[b, h, i, d] = math.fsum(e[t] * v[b, hk, j, d]
+                                              for t, j in enumerate(keys)) / tot
                 L[b, h, i] = mx + math.log(tot)
     return O, L
 
@@ -262,10 +269,107 @@ def pin_row_subset(orc):
         assert np.allclose(Ls, L[:, :, rows], rtol=0, atol=1e-15)
 
 
+def pin_bruteforce_groups_alibi(orc):
+    """Brute force with grouped K/V heads (R8) and ALiBi slopes (R9)."""
+    cases = [(1, 4, 9, 4, 2, 0.5), (2, 4, 7, 3, 1, 0.3), (1, 6, 8, 5, 3, 1.0)]
+    for ci, (B, H, S, D, Hkv, sc) in enumerate(cases):
+        q = _rand((B, H, S, D), 40 + ci)
+        k = _rand((B, Hkv, S, D), 50 + ci)
+        v = _rand((B, Hkv, S, D), 60 + ci)
+        slopes = np.linspace(0.05, 0.9, H)
+        for causal, w, ns in MASKS[:4]:
+            for sl in (None, slopes):
+                O, L = orc.attention_fwd(q, k, v, causal=causal, scale=sc, window=w, n_sink=ns,
+                                         alibi_slopes=sl)
+                Ob, Lb = _brute(q, k, v, causal, sc, w, ns, sl)
+                assert np.allclose(O, Ob, rtol=0, atol=1e-12), (ci, causal, w, ns)
+                assert np.allclose(L, Lb, rtol=0, atol=1e-12), (ci, causal, w, ns)
+
+
+def pin_groups_equal_repeated_heads(orc):
+    """Grouped K/V heads (R8) are ordinary attention over K/V heads repeated
+    G = Hq / Hkv times in a row (the deck's MQA is the case Hkv = 1)."""
+    B, H, S, D = 2, 8, 33, 8
+    q = _rand((B, H, S, D), 70)
+    for Hkv in (1, 2, 4, 8):
+        k = _rand((B, Hkv, S, D), 71)
+        v = _rand((B, Hkv, S, D), 72)
+        G = H // Hkv
+        for causal, w, ns in MASKS[:3]:
+            O, L = orc.attention_fwd(q, k, v, causal=causal, scale=0.4, window=w, n_sink=ns)
+            Or, Lr = orc.attention_fwd(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1),
+                                       causal=causal, scale=0.4, window=w, n_sink=ns)
+            assert np.array_equal(O, Or) and np.array_equal(L, Lr), (Hkv, causal)
+
+
+def pin_alibi_slope_rule(orc):
+    """The deck's slope rule for H = 4, as the golden file writes it out."""
+    g = json.loads((GOLDEN / "lesson91_alibi_slopes.json").read_text())
+    assert np.array_equal(orc.alibi_slopes(g["H"]), np.array(g["slopes"]))
+    for H in (1, 8, 12, 32):
+        m = orc.alibi_slopes(H)
+        assert m.shape == (H,) and math.isclose(m[-1], 2.0 ** -8) and np.all(np.diff(m) < 0)
+
+
+def pin_alibi_closed_form(orc):
+    """At scale 0 the logits are -m|i - j| alone, so P is a truncated geometric
+    distribution: with V the identity (D = S), O[i, j] = P[i, j] exactly, and
+    LSE_i = log of the geometric sum over the visible keys."""
+    S = 24
+    q = _rand((1, 2, S, S), 80)
+    k = _rand((1, 2, S, S), 81)
+    v = np.eye(S)[None, None].repeat(2, axis=1)
+    m = np.array([0.7, 0.125], dtype=np.float32)
+    for causal in (True, False):
+        O, L = orc.attention_fwd(q, k, v, causal=causal, scale=0.0, alibi_slopes=m)
+        for h in range(2):
+            r = math.exp(-float(m[h]))
+            for i in range(S):
+                js = range(i + 1) if causal else range(S)
+                tot = math.fsum(r ** abs(i - j) for j in js)
+                want = np.zeros(S)
+                for j in js:
+                    want[j] = r ** abs(i - j) / tot
+                assert np.allclose(O[0, h, i], want, rtol=0, atol=1e-13), (causal, h, i)
+                assert math.isclose(L[0, h, i], math.log(tot), rel_tol=0, abs_tol=1e-13)
+
+
+def pin_alibi_sdpa_library(orc):
+    """ALiBi as an additive float mask in torch's scaled_dot_product_attention
+    (CPU, fp64), together with the causal / window mask as -inf."""
+    B, H, S, D = 1, 4, 40, 16
+    q, k, v = _qkv(B, H, S, D, 90)
+    slopes = orc.alibi_slopes(H).astype(np.float32).astype(np.float64)
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    for causal, w, ns in MASKS[:4]:
+        keep = orc.visible(np.arange(S), S, causal, w, ns)
+        bias = -slopes[:, None, None] * np.abs(i - j)[None] + np.where(keep, 0.0, -np.inf)[None]
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                             torch.from_numpy(v),
+                                             attn_mask=torch.from_numpy(bias)[None],
+                                             scale=float(np.float32(0.25))).numpy()
+        O, _ = orc.attention_fwd(q, k, v, causal=causal, scale=0.25, window=w, n_sink=ns,
+                                 alibi_slopes=orc.alibi_slopes(H))
+        assert np.allclose(O, ref, rtol=0, atol=1e-12), (causal, w, ns)
+
+
+def pin_alibi_zero_slopes(orc):
+    """Zero slopes leave ordinary attention, bit for bit."""
+    q, k, v = _qkv(1, 3, 20, 8, 95)
+    for causal, w, ns in MASKS[:4]:
+        a = orc.attention_fwd(q, k, v, causal=causal, scale=0.3, window=w, n_sink=ns)
+        b = orc.attention_fwd(q, k, v, causal=causal, scale=0.3, window=w, n_sink=ns,
+                              alibi_slopes=np.zeros(3))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 PINS = [pin_bruteforce, pin_probs, pin_constant_v, pin_causal_row0, pin_prefix_independence,
         pin_tiled_block_invariance, pin_lab3_worked_example, pin_sdpa_library,
         pin_closed_form_scale0, pin_window_degenerate, pin_shift_invariance,
-        pin_permutation_noncausal, pin_row_subset]
+        pin_permutation_noncausal, pin_row_subset, pin_bruteforce_groups_alibi,
+        pin_groups_equal_repeated_heads, pin_alibi_slope_rule, pin_alibi_closed_form,
+        pin_alibi_sdpa_library, pin_alibi_zero_slopes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -345,23 +449,39 @@ MUTATIONS = {
     "sinks_dropped": ("keep = keep & (in_window | is_sink)", "keep = keep & in_window"),
     "sinks_ignore_causality": ("keep = keep & (in_window | is_sink)",
                                "keep = (keep & in_window) | is_sink"),
-    "scale_dropped": ("@ k[b, h].T) * s ", "@ k[b, h].T) "),
+    "scale_dropped": ("@ k[b, g].T) * s ", "@ k[b, g].T) "),
     "scale_not_fp32": ("return float(np.float32(scale))", "return float(scale)"),
-    "operands_swapped": ("(q[b, h, rr, :] @ k[b, h].T)", "(k[b, h, rr, :] @ q[b, h].T)"),
-    "no_normalisation": ("(p @ v[b, h]) / l_safe[:, None]", "(p @ v[b, h])"),
+    "operands_swapped": ("(q[b, h, rr, :] @ k[b, g].T)", "(k[b, g, rr, :] @ q[b, h].T)"),
+    "no_normalisation": ("(p @ v[b, g]) / l_safe[:, None]", "(p @ v[b, g])"),
     "lse_log2": ("m + np.log(l_safe)", "m + np.log2(l_safe)"),
     "lse_without_max": ("m + np.log(l_safe)", "np.log(l_safe)"),
     "no_max_subtraction": ("p = np.exp(scores - m_safe[:, None])", "p = np.exp(scores)"),
-    "v_rows_misaligned": ("(p @ v[b, h])", "(p @ np.roll(v[b, h], 1, axis=0))"),
+    "v_rows_misaligned": ("(p @ v[b, g])", "(p @ np.roll(v[b, g], 1, axis=0))"),
+    "kv_heads_interleaved": ("return h // (Hq // Hkv)", "return h % Hkv"),
+    "alibi_sign": ("scores = scores - slopes[h] * dist", "scores = scores + slopes[h] * dist"),
+    "alibi_signed_distance": ("dist = np.abs(rr[:, None] - j_idx)", "dist = (rr[:, None] - j_idx)"),
+    "alibi_slopes_from_zero": ("for h in range(1, H + 1)", "for h in range(H)"),
+    "alibi_wrong_head": ("scores = scores - slopes[h] * dist",
+                         "scores = scores - slopes[g] * dist"),
+    # the deck's trap (slide 28): the bias added to the probabilities, after the softmax
+    "alibi_after_softmax": [("scores = scores - slopes[h] * dist", "pass"),
+                            ("P[b, h, c0:c0 + rr.size] = p / l_safe[:, None]",
+                             "P[b, h, c0:c0 + rr.size] = p / l_safe[:, None] - "
+                             "(0.0 if slopes is None else slopes[h] * dist)"),
+                            ("O[b, h, c0:c0 + rr.size] = (p @ v[b, g]) / l_safe[:, None]",
+                             "O[b, h, c0:c0 + rr.size] = ((p / l_safe[:, None] - "
+                             "(0.0 if slopes is None else slopes[h] * dist)) @ v[b, g])")],
 }
 
 
 def _mutant(name):
     src = pathlib.Path(ORACLE.__file__).read_text()
-    old, new = MUTATIONS[name]
-    assert src.count(old) >= 1, name
+    edits = MUTATIONS[name]
+    for old, new in ([edits] if isinstance(edits, tuple) else edits):
+        assert src.count(old) >= 1, (name, old)
+        src = src.replace(old, new)
     mod = types.ModuleType(f"oracle_mutant_{name}")
-    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
     return mod
 
 
