@@ -86,6 +86,36 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream, int dtype);
 
 /*
+ * flash_attn_fwd_ext -- flash_attn_fwd with grouped key/value heads and an
+ * optional ALiBi bias.
+ *
+ * Grouped heads ("Lesson 91" deck, slide 32 "MQA: one shared K, V for all
+ * query heads", and its note on grouped-query attention): q and o hold H
+ * query heads, k and v hold H_kv key/value heads, and query head h reads
+ * key/value head h / (H / H_kv) -- consecutive query heads form the groups.
+ * H_kv = 1 is multi-query attention, H_kv = H ordinary attention.
+ *
+ * ALiBi (same deck, slides 20-25 and 28): if alibi_slopes is non-NULL, the
+ * logit of (i, j) in query head h is scale * Q_i.K_j - alibi_slopes[h] * |i - j|,
+ * the bias added before the softmax (and so inside the logsumexp). The deck's
+ * slopes are 2^(-8 h'/H) for h' = h + 1; any finite slopes are accepted.
+ *
+ * q, o    : device pointers, [B, H, S, D], `dtype`, 16-byte aligned.
+ * k, v    : device pointers, [B, H_kv, S, D], `dtype`, 16-byte aligned.
+ * lse     : device pointer, [B, H, S] fp32, 4-byte aligned.
+ * H_kv    : >= 1 and a divisor of H.
+ * alibi_slopes : device pointer to H fp32 slopes (4-byte aligned), or NULL for
+ *           no bias. Read only; must not overlap o or lse.
+ * Everything else, the precision, ownership, timing and errors are those of
+ * flash_attn_fwd, plus FA_ERR_INVALID for H_kv < 1, H_kv not dividing H, a
+ * misaligned or overlapping alibi_slopes.
+ */
+int flash_attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                       int causal, int64_t window, int64_t n_sink, float scale,
+                       const float* alibi_slopes, void* stream, int dtype);
+
+/*
  * flash_attn_fwd_counted -- flash_attn_fwd plus an instrumentation counter.
  *
  * block_pairs : device pointer to one uint64 (8-byte aligned), or NULL. When

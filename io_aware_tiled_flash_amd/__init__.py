@@ -36,6 +36,9 @@ class _CAPI:
         fwd_args = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, i64, f32, vp, i32]
         self.flash_attn_fwd = self._fn("flash_attn_fwd", fwd_args, i32)
         self.flash_attn_fwd_counted = self._fn("flash_attn_fwd_counted", fwd_args + [vp], i32)
+        self.flash_attn_fwd_ext = self._fn(
+            "flash_attn_fwd_ext",
+            [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp, vp, i32], i32)
         self.flash_attn_tile_shape = self._fn(
             "flash_attn_tile_shape",
             [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
@@ -96,7 +99,7 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs):
+def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alibi_slopes=None):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
@@ -105,13 +108,19 @@ def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, H, S, D]")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share the shape [B, H, S, D]")
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H_kv, S, D] with q's B, S, D")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one device")
-    B, H, S, D = q.shape
+    if alibi_slopes is not None:
+        if not isinstance(alibi_slopes, torch.Tensor) or alibi_slopes.dtype != torch.float32 \
+                or alibi_slopes.shape != (H,) or not alibi_slopes.is_contiguous() \
+                or alibi_slopes.device != q.device:
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor [H] on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
@@ -123,29 +132,40 @@ def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, S] on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
-                B, H, S, D, int(bool(causal)), int(window), int(n_sink), float(scale),
-                stream, _dtype_code(q))
-        if block_pairs is None:
-            rc = capi().flash_attn_fwd(*args)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr())
+        mask = (int(bool(causal)), int(window), int(n_sink), float(scale))
+        if Hkv != H or alibi_slopes is not None:
+            if block_pairs is not None:
+                raise ValueError("the block counter is available for plain multi-head calls only")
+            slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+            rc = capi().flash_attn_fwd_ext(*ptrs, B, H, Hkv, S, D, *mask, slopes, stream,
+                                           _dtype_code(q))
+        elif block_pairs is None:
+            rc = capi().flash_attn_fwd(*ptrs, B, H, S, D, *mask, stream, _dtype_code(q))
         else:
             if block_pairs.dtype not in (torch.int64, torch.uint64) or block_pairs.numel() < 1 \
                     or not block_pairs.is_cuda:
                 raise ValueError("block_pairs must be a GPU int64 tensor")
-            rc = capi().flash_attn_fwd_counted(*args, block_pairs.data_ptr())
+            rc = capi().flash_attn_fwd_counted(*ptrs, B, H, S, D, *mask, stream, _dtype_code(q),
+                                               block_pairs.data_ptr())
     _check(rc)
     return o, l
 
 
 def flash_attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, n_sink: int = 0,
-                   scale: float | None = None, out=None, lse=None):
+                   scale: float | None = None, alibi_slopes=None, out=None, lse=None):
     """Attention forward on the GPU: returns (o [B,H,S,D] in q's dtype, lse [B,H,S] fp32).
 
-    q, k, v: contiguous GPU tensors [B, H, S, D] of one dtype (float32, float16,
-    bfloat16). scale defaults to 1/sqrt(D); window/n_sink need causal=True.
-    Enqueued on torch's current stream; no synchronisation happens here.
+    q: contiguous GPU tensor [B, H, S, D]; k, v: [B, H_kv, S, D] with H_kv
+    dividing H (query head h reads key/value head h // (H // H_kv); H_kv = 1 is
+    multi-query attention); one dtype (float32, float16, bfloat16). scale
+    defaults to 1/sqrt(D); window/n_sink need causal=True. alibi_slopes: an
+    optional contiguous float32 GPU tensor [H]; the logit of (i, j) in head h
+    then gains -alibi_slopes[h] * |i - j| (the Lesson 91 deck's slopes are
+    2^(-8 (h + 1) / H)). Enqueued on torch's current stream; no
+    synchronisation happens here.
     """
-    return _forward(q, k, v, causal, window, n_sink, scale, out, lse, None)
+    return _forward(q, k, v, causal, window, n_sink, scale, out, lse, None, alibi_slopes)
 
 
 def flash_attn_fwd_counted(q, k, v, block_pairs, *, causal: bool = False, window: int = 0,

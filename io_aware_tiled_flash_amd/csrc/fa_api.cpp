@@ -41,11 +41,13 @@ int elem_bytes(int dtype) {
 bool supported_d(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
 int forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-            int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink, float scale,
-            void* stream, int dtype, uint64_t* block_pairs) {
+            int64_t Hkv, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
+            float scale, const float* alibi, void* stream, int dtype, uint64_t* block_pairs) {
   g_last_error.clear();
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID, "null tensor pointer");
   if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_INVALID, "B, H and S must be >= 1");
+  if (Hkv < 1 || H % Hkv != 0)
+    return fail(FA_ERR_INVALID, "key/value heads must be >= 1 and divide the query heads");
   if (D < 1) return fail(FA_ERR_INVALID, "D must be >= 1");
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1");
   if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
@@ -59,6 +61,7 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (!aligned(lse, 4)) return fail(FA_ERR_INVALID, "lse must be 4-byte aligned");
   if (block_pairs && !aligned(block_pairs, 8))
     return fail(FA_ERR_INVALID, "block_pairs must be 8-byte aligned");
+  if (alibi && !aligned(alibi, 4)) return fail(FA_ERR_INVALID, "alibi_slopes must be 4-byte aligned");
   // Byte sizes must fit in int64: B*H*S*D*e.
   const int64_t lim = INT64_MAX;
   if (B > lim / H) return fail(FA_ERR_INVALID, "B*H overflows");
@@ -66,12 +69,16 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (bh > lim / S) return fail(FA_ERR_INVALID, "B*H*S overflows");
   const int64_t rows = bh * S;
   if (rows > lim / D || rows * D > lim / e) return fail(FA_ERR_INVALID, "tensor size overflows");
-  const uint64_t tbytes = (uint64_t)(rows * D * e);
-  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
-      overlaps(o, tbytes, v, tbytes))
+  const uint64_t tbytes = (uint64_t)(rows * D * e);            // q and o
+  const uint64_t kvbytes = tbytes / (uint64_t)(H / Hkv);        // k and v
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, kvbytes) ||
+      overlaps(o, tbytes, v, kvbytes))
     return fail(FA_ERR_INVALID, "o overlaps q, k or v");
   if (overlaps(lse, (uint64_t)rows * 4, o, tbytes))
     return fail(FA_ERR_INVALID, "lse overlaps o");
+  if (alibi && (overlaps(alibi, (uint64_t)H * 4, o, tbytes) ||
+                overlaps(alibi, (uint64_t)H * 4, lse, (uint64_t)rows * 4)))
+    return fail(FA_ERR_INVALID, "alibi_slopes overlaps o or lse");
 
   if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
   const fa::Plan plan = fa::plan_fwd(B * H, S, D, dtype);
@@ -87,8 +94,11 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.o = o;
   p.lse = lse;
   p.block_pairs = reinterpret_cast<unsigned long long*>(block_pairs);
+  p.alibi = alibi;
   p.S = (int)S;
   p.BH = (int)bh;
+  p.H = (int)H;
+  p.G = (int)(H / Hkv);
   p.nqb = (int)nqb;
   p.causal = causal;
   // A window as wide as the sequence hides nothing: fold it to "no window".
@@ -156,16 +166,24 @@ extern "C" {
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                    int64_t H, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
                    float scale, void* stream, int dtype) {
-  return forward(q, k, v, o, lse, B, H, S, D, causal, window, n_sink, scale, stream, dtype,
-                 nullptr);
+  return forward(q, k, v, o, lse, B, H, H, S, D, causal, window, n_sink, scale, nullptr, stream,
+                 dtype, nullptr);
+}
+
+int flash_attn_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                       int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window,
+                       int64_t n_sink, float scale, const float* alibi_slopes, void* stream,
+                       int dtype) {
+  return forward(q, k, v, o, lse, B, H, H_kv, S, D, causal, window, n_sink, scale, alibi_slopes,
+                 stream, dtype, nullptr);
 }
 
 int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,
                            int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t window,
                            int64_t n_sink, float scale, void* stream, int dtype,
                            uint64_t* block_pairs) {
-  return forward(q, k, v, o, lse, B, H, S, D, causal, window, n_sink, scale, stream, dtype,
-                 block_pairs);
+  return forward(q, k, v, o, lse, B, H, H, S, D, causal, window, n_sink, scale, nullptr, stream,
+                 dtype, block_pairs);
 }
 
 int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,

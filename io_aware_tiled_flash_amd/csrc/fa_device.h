@@ -106,14 +106,34 @@ __device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, 
 }
 
 // Work-group -> (query block, batch*head). Heaviest query blocks first under
-// the causal mask; consecutive ids walk over heads so that, with B*H a
-// multiple of 8, every query block of a head runs on the same XCD (the
-// dispatcher deals work-group ids round-robin over the 8 XCDs).
+// the causal mask. Consecutive ids walk over heads, and the dispatcher deals
+// ids round-robin over the 8 XCDs, so with B*H a multiple of 8 every query
+// block of a head runs on one XCD; the heads are spread so that each XCD
+// holds a contiguous run of them, which keeps query heads that share a
+// key/value head (consecutive heads) on one XCD's L2 as well.
 __device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
   const int id = blockIdx.x;
-  bh = id % p.BH;
+  const int x = id % p.BH;
   const int rank = id / p.BH;
+  bh = (p.BH & 7) ? x : (x & 7) * (p.BH >> 3) + (x >> 3);
   qb = p.causal ? (p.nqb - 1 - rank) : rank;
 }
+
+// ALiBi bias in the base-2 logit domain: turns raw (sign-folded) scores into
+// t = c * s - b2 * |i - j| for keys j = jb + e, e = 32 t + 8 (r >> 2) + (r & 3),
+// with b2 = slope * log2(e). The softmax then runs on t with a unit scale.
+template <int NT>
+__device__ __forceinline__ void alibi_logits(f32x16 (&acc)[NT], float c, float b2, int i, int jb) {
+  const float d0 = (float)(i - jb);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = (float)(32 * t + 8 * (r >> 2) + (r & 3));
+      acc[t][r] = __builtin_fmaf(acc[t][r], c, -b2 * fabsf(d0 - e));
+    }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace fa

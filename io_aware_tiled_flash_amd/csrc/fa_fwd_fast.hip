@@ -137,7 +137,7 @@ __device__ __forceinline__ u32x2 lds_tr_read(const T* p) {
 // owns 32 query rows; lane (col, h) = (lane & 31, lane >> 5) owns query row
 // i = q_lo + 32 * wave_in_block + col and, in every 32-key sub-tile, the keys
 // 8 g + 4 h + r (g, r < 4) of the S^T accumulator.
-template <typename T, int D, int BR>
+template <typename T, int D, int BR, bool ALIBI>
 struct Core {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
@@ -153,11 +153,13 @@ struct Core {
   float m_run;       // running max (raw sign-folded score units)
   float mc;          // m_run * c, or 0 while nothing is visible
   float l[4];        // this lane half's running sum, in 4 parts
-  float c, tau_raw;
+  float c, tau_raw;  // softmax scale (1 when ALiBi logits are already scaled)
+  float b2;          // ALiBi slope in base 2 (ALIBI only)
   int i, h, col;
 
   __device__ __forceinline__ void init(const FwdParams& p, const T* __restrict__ Qh, int q_row,
-                                       int lane) {
+                                       int lane, int bh) {
+    b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
     h = lane >> 5;
     col = lane & 31;
     i = q_row;
@@ -185,7 +187,7 @@ struct Core {
     mc = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) l[k] = 0.f;
-    c = p.c;
+    c = ALIBI ? 1.f : p.c;
     tau_raw = kTau / c;
   }
 
@@ -321,12 +323,12 @@ struct Core {
 // being read and does not wait for the in-flight loads before each read (it
 // would have to if both were slots of one array picked at run time).
 // ------------------------------------------------------------------------ //
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, bool ALIBI>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fast_kernel(FwdParams p) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kBCf;
-  using C = Core<T, D, BR>;
+  using C = Core<T, D, BR, ALIBI>;
   constexpr int TILE = BC * D;
 
   __shared__ __attribute__((aligned(1024))) T k0s[TILE];
@@ -343,9 +345,10 @@ void fa_fwd_fast_kernel(FwdParams p) {
   const int S = p.S;
   const int q_lo = qb * BR;
   const size_t head = (size_t)bh * (size_t)S * D;
+  const size_t kv_head = (size_t)(bh / p.G) * (size_t)S * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + head;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + head;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
 
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_iter = br.count();
@@ -361,7 +364,7 @@ void fa_fwd_fast_kernel(FwdParams p) {
   vdma.load(v0s, Vh, br.kb(0) * BC, S, wave);
 
   C core;
-  core.init(p, Qh, q_lo + 32 * wave + (lane & 31), lane);
+  core.init(p, Qh, q_lo + 32 * wave + (lane & 31), lane, bh);
 
   wait_vmem<0>();
   __syncthreads();
@@ -386,6 +389,7 @@ void fa_fwd_fast_kernel(FwdParams p) {
     f32x16 sacc[C::NT];
     core.qk(sacc, kc);
     if (decltype(mask)::value) core.mask(sacc, p, br.kb(it) * BC);
+    if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, br.kb(it) * BC + 4 * core.h);
     typename C::v8 pb[C::NT][2];
     core.softmax(sacc, pb);
     core.pv(vc, pb);
@@ -422,13 +426,37 @@ bool fast_supported(int D, int dtype) {
 }
 int fast_tile_keys() { return kBCf; }
 
-template <typename T, int D>
-static hipError_t launch_fast_t(const FwdParams& p, int nw, hipStream_t st) {
+// Explicit instantiations: with several instantiations of the kernel template
+// in one translation unit, the host pass emitted launch stubs only for the
+// first boolean variant it met; naming each one here makes all of them exist.
+#define FA_FAST_INST(T, D, NW)                                             \
+  template __global__ void fa_fwd_fast_kernel<T, D, NW, false>(FwdParams); \
+  template __global__ void fa_fwd_fast_kernel<T, D, NW, true>(FwdParams);
+FA_FAST_INST(__bf16, 128, 8)
+FA_FAST_INST(__bf16, 128, 4)
+FA_FAST_INST(__bf16, 64, 8)
+FA_FAST_INST(__bf16, 64, 4)
+FA_FAST_INST(_Float16, 128, 8)
+FA_FAST_INST(_Float16, 128, 4)
+FA_FAST_INST(_Float16, 64, 8)
+FA_FAST_INST(_Float16, 64, 4)
+#undef FA_FAST_INST
+
+template <typename T, int D, bool ALIBI>
+static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH;
   if (nw == 8)
-    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8>), dim3(grid), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, ALIBI>), dim3(grid), dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 4>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 4, ALIBI>), dim3(grid), dim3(256), 0, st, p);
+}
+
+template <typename T, int D>
+static hipError_t launch_fast_t(const FwdParams& p, int nw, hipStream_t st) {
+  if (p.alibi)
+    launch_fast_a<T, D, true>(p, nw, st);
+  else
+    launch_fast_a<T, D, false>(p, nw, st);
   return hipGetLastError();
 }
 

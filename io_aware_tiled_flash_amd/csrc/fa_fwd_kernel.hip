@@ -53,11 +53,13 @@ constexpr int kBC = 64;            // keys per streamed block
 // Online-softmax update for one K block, shared by both element paths.
 // sacc[t][r] holds raw scores (sign-folded Q . K) for keys
 //   j = k0 + 32 t + 8 (r >> 2) + 4 h + (r & 3)   of query row i.
-// Turns them into p = exp2(c s - m2) in place and returns alpha.
+// Turns them into p = exp2(c s - m2) in place and returns alpha. With ALIBI
+// the scores first become base-2 logits c s - b2 |i - j| and the rest runs
+// with a unit scale.
 // ------------------------------------------------------------------------ //
-template <int NT>
+template <int NT, bool ALIBI>
 __device__ __forceinline__ float softmax_step(f32x16 (&sacc)[NT], bool full, int i, int k0, int h,
-                                              const FwdParams& p, float& m2, float& l) {
+                                              const FwdParams& p, float b2, float& m2, float& l) {
   if (!full) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -68,13 +70,14 @@ __device__ __forceinline__ float softmax_step(f32x16 (&sacc)[NT], bool full, int
         sacc[t][r] = keep_ij(i, j, p.S, p.causal, p.window, p.n_sink) ? x : kNegInf;
       }
   }
+  if (ALIBI) alibi_logits<NT>(sacc, p.c, b2, i, k0 + 4 * h);
   float mt = sacc[0][0];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[t][r]);
   mt = xhalf_max(mt);
-  const float c = p.c;
+  const float c = ALIBI ? 1.f : p.c;
   float m2_new = fmaxf(m2, mt * c);                 // c > 0, so c*max = max of c*s
   float m2_use = (m2_new == kNegInf) ? 0.f : m2_new;
   float alpha = fast_exp2(m2 - m2_use);             // m2 = -inf (nothing seen) -> 0
@@ -95,7 +98,7 @@ __device__ __forceinline__ float softmax_step(f32x16 (&sacc)[NT], bool full, int
 // ------------------------------------------------------------------------ //
 // bf16 / f16 kernel.
 // ------------------------------------------------------------------------ //
-template <typename T, int D>
+template <typename T, int D, bool ALIBI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_half_kernel(FwdParams p) {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
@@ -125,9 +128,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int q_lo = qb * kBR;
   const int i = q_lo + 32 * wave + col;   // this lane's query row
   const size_t head = (size_t)bh * (size_t)S * D;
+  const size_t kv_head = (size_t)(bh / p.G) * (size_t)S * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + head;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + head;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
+  const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
 
   if (D < 32) {   // O^T rows d >= D read zeros from V^T
     for (int e = tid; e < 2 * DP * VSTR; e += kThreads) (&Vt[0][0])[e] = T(0.f);
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 
     const bool full = block_full<kBR, kBC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
-    const float alpha = softmax_step<NT>(sacc, full, i, k0, h, p, m2, l);
+    const float alpha = softmax_step<NT, ALIBI>(sacc, full, i, k0, h, p, b2, m2, l);
 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 //    exactly the accumulator's own key for that register; V^T keeps, per
 //    32-key chunk, keys {8g + 4h + r} of half h at 16h + 4g + r.
 // ------------------------------------------------------------------------ //
-template <int D>
+template <int D, bool ALIBI>
 __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int KSTR = D + 4;
@@ -340,9 +345,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
   const int q_lo = qb * kBR;
   const int i = q_lo + 32 * wave + col;
   const size_t head = (size_t)bh * (size_t)S * D;
+  const size_t kv_head = (size_t)(bh / p.G) * (size_t)S * D;
   const float* __restrict__ Qh = reinterpret_cast<const float*>(p.q) + head;
-  const float* __restrict__ Kh = reinterpret_cast<const float*>(p.k) + head;
-  const float* __restrict__ Vh = reinterpret_cast<const float*>(p.v) + head;
+  const float* __restrict__ Kh = reinterpret_cast<const float*>(p.k) + kv_head;
+  const float* __restrict__ Vh = reinterpret_cast<const float*>(p.v) + kv_head;
+  const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
 
   if (D < 32) {
     for (int e = tid; e < 2 * DP * VSTR; e += kThreads) (&Vt[0][0])[e] = 0.f;
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
     }
 
     const bool full = block_full<kBR, kBC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
-    const float alpha = softmax_step<NT>(sacc, full, i, k0, h, p, m2, l);
+    const float alpha = softmax_step<NT, ALIBI>(sacc, full, i, k0, h, p, b2, m2, l);
 
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -504,35 +511,43 @@ static hipError_t launch_kernel(K kernel, const FwdParams& p, unsigned grid, hip
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool ALIBI>
 static hipError_t launch_half(const FwdParams& p, int D, unsigned grid, hipStream_t st) {
   switch (D) {
-    case 16: return launch_kernel(fa_fwd_half_kernel<T, 16>, p, grid, st);
-    case 32: return launch_kernel(fa_fwd_half_kernel<T, 32>, p, grid, st);
-    case 64: return launch_kernel(fa_fwd_half_kernel<T, 64>, p, grid, st);
-    case 128: return launch_kernel(fa_fwd_half_kernel<T, 128>, p, grid, st);
+    case 16: return launch_kernel(fa_fwd_half_kernel<T, 16, ALIBI>, p, grid, st);
+    case 32: return launch_kernel(fa_fwd_half_kernel<T, 32, ALIBI>, p, grid, st);
+    case 64: return launch_kernel(fa_fwd_half_kernel<T, 64, ALIBI>, p, grid, st);
+    case 128: return launch_kernel(fa_fwd_half_kernel<T, 128, ALIBI>, p, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <bool ALIBI>
 static hipError_t launch_f32(const FwdParams& p, int D, unsigned grid, hipStream_t st) {
   switch (D) {
-    case 16: return launch_kernel(fa_fwd_f32_kernel<16>, p, grid, st);
-    case 32: return launch_kernel(fa_fwd_f32_kernel<32>, p, grid, st);
-    case 64: return launch_kernel(fa_fwd_f32_kernel<64>, p, grid, st);
-    case 128: return launch_kernel(fa_fwd_f32_kernel<128>, p, grid, st);
+    case 16: return launch_kernel(fa_fwd_f32_kernel<16, ALIBI>, p, grid, st);
+    case 32: return launch_kernel(fa_fwd_f32_kernel<32, ALIBI>, p, grid, st);
+    case 64: return launch_kernel(fa_fwd_f32_kernel<64, ALIBI>, p, grid, st);
+    case 128: return launch_kernel(fa_fwd_f32_kernel<128, ALIBI>, p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool ALIBI>
+static hipError_t launch_generic_a(const FwdParams& p, int D, int dtype, unsigned grid,
+                                   hipStream_t st) {
+  switch (dtype) {
+    case kDtypeBF16: return launch_half<__bf16, ALIBI>(p, D, grid, st);
+    case kDtypeF16: return launch_half<_Float16, ALIBI>(p, D, grid, st);
+    case kDtypeF32: return launch_f32<ALIBI>(p, D, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_generic(const FwdParams& p, int D, int dtype, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH;
-  switch (dtype) {
-    case kDtypeBF16: return launch_half<__bf16>(p, D, grid, st);
-    case kDtypeF16: return launch_half<_Float16>(p, D, grid, st);
-    case kDtypeF32: return launch_f32(p, D, grid, st);
-    default: return hipErrorInvalidValue;
-  }
+  return p.alibi ? launch_generic_a<true>(p, D, dtype, grid, st)
+                 : launch_generic_a<false>(p, D, dtype, grid, st);
 }
 
 }  // namespace fa

@@ -11,6 +11,7 @@ enum { kDtypeF32 = 0, kDtypeF16 = 1, kDtypeBF16 = 2 };
 // Arguments of one forward launch, already validated and normalised on the
 // host: window >= S is folded to 0 (no window), n_sink is clamped to S, and a
 // negative scale is folded into the sign of Q (neg = 1) so that c > 0.
+// Query head bh (= b * H + h) reads key/value head bh / G.
 struct FwdParams {
   const void* q;
   const void* k;
@@ -18,8 +19,11 @@ struct FwdParams {
   void* o;
   float* lse;
   unsigned long long* block_pairs;  // optional instrumentation counter (may be null)
+  const float* alibi;  // per-query-head ALiBi slopes [H], or null (no bias)
   int S;        // sequence length
-  int BH;       // batch * heads
+  int BH;       // batch * query heads
+  int H;        // query heads
+  int G;        // query heads per key/value head
   int nqb;      // query blocks per head = ceil(S / block_q of the chosen kernel)
   int causal;   // 0 / 1
   int window;   // 0 = none

@@ -33,8 +33,8 @@ def _declared_functions():
 
 def test_headers_declare_the_abi():
     names = _declared_functions()
-    assert {"flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_tile_shape",
-            "flash_attn_last_error", "flash_attn_version"} <= names
+    assert {"flash_attn_fwd", "flash_attn_fwd_ext", "flash_attn_fwd_counted",
+            "flash_attn_tile_shape", "flash_attn_last_error", "flash_attn_version"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -111,6 +111,38 @@ def test_invalid_arguments_rejected(case):
     rc, msg = _call(**INVALID[case])
     assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
     assert msg
+
+
+def _call_ext(q=Q, k=K, v=V, o=O, lse=L, B=1, H=4, H_kv=2, S=64, D=64, causal=1, window=0,
+              n_sink=0, scale=0.125, alibi=None, stream=None, dtype=fa.FA_BF16):
+    rc = fa.capi().flash_attn_fwd_ext(q, k, v, o, lse, B, H, H_kv, S, D, causal, window, n_sink,
+                                      scale, alibi, stream, dtype)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID_EXT = {
+    "kv_heads_zero": dict(H_kv=0),
+    "kv_heads_negative": dict(H_kv=-2),
+    "kv_heads_not_dividing": dict(H=6, H_kv=4),
+    "kv_heads_above_heads": dict(H=2, H_kv=4),
+    "alibi_misaligned": dict(alibi=0x600002),
+    "alibi_overlaps_o": dict(alibi=O + 64),
+    "alibi_overlaps_lse": dict(alibi=L),
+    "null_k_ext": dict(k=None),
+    "window_without_causal_ext": dict(causal=0, window=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID_EXT))
+def test_invalid_ext_arguments_rejected(case):
+    rc, msg = _call_ext(**INVALID_EXT[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+    assert msg
+
+
+def test_ext_unsupported_head_dim():
+    rc, msg = _call_ext(D=96)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "head dim" in msg
 
 
 @pytest.mark.parametrize("D", [8, 48, 96, 256, 512])

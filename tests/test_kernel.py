@@ -45,17 +45,22 @@ def gpu_fwd(q, k, v, **kw):
 
 
 def compare(o, lse, q, k, v, dtype, *, causal, scale, window=0, n_sink=0, heads=None,
-            rows=None, label="", tol_o=None):
+            rows=None, label="", tol_o=None, alibi=None):
     """o, lse: GPU results (device tensors). heads: list of (b, h) to check
-    (default all); rows: query rows to check (default all)."""
+    (default all); rows: query rows to check (default all). k, v may hold fewer
+    heads than q (grouped heads); alibi: optional per-head slopes (numpy)."""
     tol_o = TOL_O[dtype] if tol_o is None else tol_o
     B, H, S, D = q.shape
+    Hkv = k.shape[1]
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     worst_o, worst_l = 0.0, 0.0
     for b, h in heads:
-        q64, k64, v64 = (fa_inputs.to_f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+        g = ORACLE.kv_head(h, H, Hkv)
+        q64 = fa_inputs.to_f64(q[b:b + 1, h:h + 1])
+        k64, v64 = (fa_inputs.to_f64(t[b:b + 1, g:g + 1]) for t in (k, v))
         O, L = ORACLE.attention_fwd(q64, k64, v64, causal=causal, scale=scale, window=window,
-                                    n_sink=n_sink, rows=rows)
+                                    n_sink=n_sink, rows=rows,
+                                    alibi_slopes=None if alibi is None else alibi[h:h + 1])
         r = slice(None) if rows is None else torch.as_tensor(np.asarray(rows))
         og = o[b, h].float().cpu()[r].double().numpy()
         lg = lse[b, h].cpu()[r].double().numpy()
@@ -268,3 +273,89 @@ def test_tiled_block_guide_example_fp32():
     o, lse = gpu_fwd(q, k, v, causal=False, scale=0.125)
     worst, _ = compare(o, lse, q, k, v, "f32", causal=False, scale=0.125, label="guide fp32")
     assert worst < 1e-4
+
+
+# --------------------------------------------------------------------------- #
+# Grouped key/value heads (MQA / GQA) and the ALiBi bias
+# --------------------------------------------------------------------------- #
+
+def _kv(B, Hkv, S, D, dtype, seed):
+    _, k, v = fa_inputs.make_qkv(B, Hkv, S, D, dtype, seed=seed)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_grouped_kv_heads(dtype, D):
+    """Query head h reads key/value head h // (H // H_kv): H = 8 with H_kv = 1
+    (multi-query), 2, 4 and 8, at B = 2 so that B*H is a multiple of 8."""
+    for S in (200, 1000):
+        q, _, _ = fa_inputs.make_qkv(2, 8, S, D, dtype, seed=S + 3)
+        for Hkv in (1, 2, 4, 8):
+            k, v = _kv(2, Hkv, S, D, dtype, seed=S + Hkv)
+            for causal, window, n_sink in MASKS[:3]:
+                scale = 1.0 / math.sqrt(D)
+                o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink,
+                                 scale=scale)
+                heads = [(b, h) for b in range(2) for h in range(8)] if S <= 200 else \
+                    [(0, 0), (0, 7), (1, 3), (1, 6)]
+                compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                        n_sink=n_sink, heads=heads,
+                        label=f"{dtype} D{D} S{S} H8/Hkv{Hkv} c{int(causal)} w{window}")
+
+
+def test_grouped_heads_equal_repeated_heads_bitwise():
+    """A grouped call and an ordinary call on explicitly repeated K/V heads run
+    the same arithmetic, so they agree bit for bit."""
+    q, _, _ = fa_inputs.make_qkv(2, 8, 333, 128, "bf16", seed=5)
+    k, v = _kv(2, 2, 333, 128, "bf16", seed=6)
+    o1, l1 = gpu_fwd(q, k, v, causal=True, scale=0.088)
+    o2, l2 = gpu_fwd(q, k.repeat_interleave(4, dim=1).contiguous(),
+                     v.repeat_interleave(4, dim=1).contiguous(), causal=True, scale=0.088)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_alibi(dtype, D):
+    """ALiBi slopes of the Lesson 91 rule (and a steep / a zero slope) under
+    every mask, alone and with grouped heads."""
+    H = 4
+    slopes = np.array(list(ORACLE.alibi_slopes(H)), dtype=np.float32)
+    steep = np.array([1.5, 0.0, 0.3, 2.0 ** -8], dtype=np.float32)
+    for S in (129, 700):
+        q, _, _ = fa_inputs.make_qkv(2, H, S, D, dtype, seed=S + 11)
+        for Hkv in (H, 2):
+            k, v = _kv(2, Hkv, S, D, dtype, seed=S + 12 + Hkv)
+            for sl in (slopes, steep):
+                sd = torch.from_numpy(sl).cuda()
+                for causal, window, n_sink in MASKS[:3]:
+                    scale = 1.0 / math.sqrt(D)
+                    o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink,
+                                     scale=scale, alibi_slopes=sd)
+                    compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                            n_sink=n_sink, alibi=sl.astype(np.float64),
+                            label=f"{dtype} D{D} S{S} alibi Hkv{Hkv} c{int(causal)} w{window}")
+
+
+def test_alibi_negative_scale_and_zero_scale():
+    """The bias is added after the (signed) scale; with scale 0 only the bias
+    remains (the oracle's geometric closed form)."""
+    H = 4
+    sl = np.array(list(ORACLE.alibi_slopes(H)), dtype=np.float32)
+    sd = torch.from_numpy(sl).cuda()
+    q, k, v = fa_inputs.make_qkv(1, H, 300, 64, "bf16", seed=21)
+    for scale in (-0.2, 0.0):
+        for causal in (False, True):
+            o, lse = gpu_fwd(q, k, v, causal=causal, scale=scale, alibi_slopes=sd)
+            compare(o, lse, q, k, v, "bf16", causal=causal, scale=scale,
+                    alibi=sl.astype(np.float64), label=f"alibi scale {scale} c{int(causal)}")
+
+
+def test_alibi_rejects_bad_slopes_tensor():
+    q, k, v = (t.cuda() for t in fa_inputs.make_qkv(1, 4, 64, 64, "bf16", seed=1))
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, k, v, alibi_slopes=torch.zeros(3, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(q, k, v, alibi_slopes=torch.zeros(4, dtype=torch.float64,
+                                                             device="cuda"))
