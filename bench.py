@@ -121,6 +121,11 @@ def kept_pairs(w) -> int:
     return tot
 
 
+def alibi_slopes(H: int):
+    """Per-head ALiBi slopes of the Lesson 91 deck (slide 23): 2^(-8h/H), h = 1..H."""
+    return [2.0 ** (-8.0 * h / H) for h in range(1, H + 1)]
+
+
 def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
     """Time the fp64 oracle on the first n_heads (b, h) heads, all rows. With
     n_heads = 0 the sample is sized from one timed head to about budget_s seconds
@@ -135,15 +140,19 @@ def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
         cores = 1
     all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
+    G = w.H // w.kv_heads
+    slopes = alibi_slopes(w.H) if w.alibi else None
+
     def head(b, h):
-        return (fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, h:h + 1]),
-                fa_inputs.to_f64(v[b:b + 1, h:h + 1]))
+        g = h // G
+        return (fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, g:g + 1]),
+                fa_inputs.to_f64(v[b:b + 1, g:g + 1]), None if slopes is None else [slopes[h]])
 
     def run(arrs):
         t0 = time.perf_counter()
-        for qq, kk, vv in arrs:
+        for qq, kk, vv, sl in arrs:
             oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale, window=w.window,
-                                 n_sink=w.n_sink)
+                                 n_sink=w.n_sink, alibi_slopes=sl)
         return time.perf_counter() - t0
 
     if n_heads <= 0:
@@ -175,7 +184,7 @@ def main():
     import io_aware_tiled_flash_amd as fa
 
     name = args.workload or fa_inputs.HEADLINE
-    w = fa_inputs.WORKLOADS[name]
+    w = fa_inputs.ALL_WORKLOADS[name]
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -186,10 +195,12 @@ def main():
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    slopes = (torch.tensor(alibi_slopes(w.H), dtype=torch.float32, device=dev)
+              if w.alibi else None)
 
     def step():
         fa.flash_attn_fwd(qd, kd, vd, causal=w.causal, window=w.window, n_sink=w.n_sink,
-                          scale=w.scale, out=o, lse=lse)
+                          scale=w.scale, alibi_slopes=slopes, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -215,7 +226,7 @@ def main():
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     e = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
-    alg_bytes = 4 * w.B * w.H * w.S * w.D * e + 4 * w.B * w.H * w.S
+    alg_bytes = (2 * w.H + 2 * w.kv_heads) * w.B * w.S * w.D * e + 4 * w.B * w.H * w.S
 
     out = {
         "metric": "attention fwd TFLOP/s & % MFMA peak (causal bf16 B4 H16 S4096 D128)",
@@ -230,7 +241,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: Q, K, V iid N(0,1), numpy default_rng(seed 0), rounded to dtype",
-        "config": {"workload": name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
+                   "alibi": w.alibi,
                    "causal": w.causal, "window": w.window, "n_sink": w.n_sink,
                    "scale": w.scale, "layout": "[B,H,S,D] contiguous",
                    "flops_per_step": flops, "nominal_flops_per_step": nominal_flops(w),

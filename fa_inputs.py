@@ -14,7 +14,8 @@ guide use.
 Recipe for a config (B, H, S, D, dtype, seed):
   rng = default_rng(seed); Q, K, V drawn in that order, each as
   rng.standard_normal((B, H, S, D), dtype=float32), then rounded to the storage
-  dtype with round-to-nearest-even (torch's `.to`).
+  dtype with round-to-nearest-even (torch's `.to`). With grouped key/value
+  heads, K and V are drawn with H_kv heads instead of H.
 The single-head fp32 worked-example config instead reproduces the Lab 3 page's
 own draw: rng.normal(size=(64, 16)) three times in float64, then cast to fp32.
 """
@@ -43,10 +44,16 @@ class Workload:
     n_sink: int = 0
     seed: int = 0
     lab3_draw: bool = False   # reproduce the Lab 3 page's (64, 16) float64 draw
+    H_kv: int = 0             # key/value heads (0: same as H)
+    alibi: bool = False       # ALiBi bias with the Lesson 91 deck's slopes
 
     @property
     def torch_dtype(self) -> torch.dtype:
         return DTYPES[self.dtype]
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
 
 # The five workloads the attention forward pass is measured and checked on.
@@ -70,18 +77,32 @@ WORKLOADS = {
 }
 HEADLINE = "causal_b4h16s4096d128_bf16"
 
+# Variants of the headline shape for the grouped-head and ALiBi extensions
+# (Lesson 91 deck: GQA with groups of 8 query heads, ALiBi slopes per head).
+EXTENSIONS = {
+    "gqa_causal_b4h16kv2s4096d128_bf16": Workload(
+        "gqa_causal_b4h16kv2s4096d128_bf16", 4, 16, 4096, 128, "bf16", True,
+        1.0 / math.sqrt(128), H_kv=2),
+    "alibi_causal_b4h16s4096d128_bf16": Workload(
+        "alibi_causal_b4h16s4096d128_bf16", 4, 16, 4096, 128, "bf16", True,
+        1.0 / math.sqrt(128), alibi=True),
+}
+ALL_WORKLOADS = {**WORKLOADS, **EXTENSIONS}
+
 
 def make_qkv(B: int, H: int, S: int, D: int, dtype: str, seed: int = 0,
-             lab3_draw: bool = False):
-    """Return (q, k, v) as contiguous CPU torch tensors [B, H, S, D] in `dtype`."""
+             lab3_draw: bool = False, H_kv: int = 0):
+    """Return (q, k, v) as contiguous CPU torch tensors in `dtype`: q [B, H, S, D],
+    k and v [B, H_kv, S, D] (H_kv = 0 means H)."""
     rng = np.random.default_rng(seed)
+    Hk = H_kv or H
     if lab3_draw:
-        if (B, H) != (1, 1):
+        if (B, H, Hk) != (1, 1, 1):
             raise ValueError("the Lab 3 draw is a single (S, D) head")
         arrs = [rng.normal(size=(S, D)) for _ in range(3)]           # float64
         arrs = [a.reshape(1, 1, S, D) for a in arrs]
     else:
-        arrs = [rng.standard_normal(size=(B, H, S, D), dtype=np.float32) for _ in range(3)]
+        arrs = [rng.standard_normal(size=(B, h, S, D), dtype=np.float32) for h in (H, Hk, Hk)]
     out = []
     for a in arrs:
         t = torch.from_numpy(np.ascontiguousarray(a)).to(DTYPES[dtype]).contiguous()
@@ -90,7 +111,7 @@ def make_qkv(B: int, H: int, S: int, D: int, dtype: str, seed: int = 0,
 
 
 def make_workload(w: Workload):
-    return make_qkv(w.B, w.H, w.S, w.D, w.dtype, w.seed, w.lab3_draw)
+    return make_qkv(w.B, w.H, w.S, w.D, w.dtype, w.seed, w.lab3_draw, w.H_kv)
 
 
 def lab3_example():

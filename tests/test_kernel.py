@@ -88,29 +88,34 @@ def _sample_rows(S, rng, n=192):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", list(fa_inputs.WORKLOADS))
+@pytest.mark.parametrize("name", list(fa_inputs.ALL_WORKLOADS))
 def test_workload_parity(name):
-    w = fa_inputs.WORKLOADS[name]
+    w = fa_inputs.ALL_WORKLOADS[name]
     _say(f"workload {name}: generating inputs")
     q, k, v = fa_inputs.make_workload(w)
+    slopes = ORACLE.alibi_slopes(w.H).astype(np.float32) if w.alibi else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
     _say(f"workload {name}: launching")
-    o, lse = gpu_fwd(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink, scale=w.scale)
+    o, lse = gpu_fwd(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink, scale=w.scale,
+                     alibi_slopes=sd)
     assert o.shape == q.shape and o.dtype == q.dtype and lse.shape == q.shape[:3]
+    al = None if slopes is None else slopes.astype(np.float64)
     small = w.B * w.H * w.S <= 32768
     if small:
         compare(o, lse, q, k, v, w.dtype, causal=w.causal, scale=w.scale, window=w.window,
-                n_sink=w.n_sink, label=name)
+                n_sink=w.n_sink, label=name, alibi=al)
     else:
         rng = np.random.default_rng(1234)
         heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]
         rows = _sample_rows(w.S, rng)
         compare(o, lse, q, k, v, w.dtype, causal=w.causal, scale=w.scale, window=w.window,
-                n_sink=w.n_sink, heads=heads, rows=rows, label=name + " (sampled rows)")
-        # properties at full size: every output finite, causal row 0 is V[0]
+                n_sink=w.n_sink, heads=heads, rows=rows, label=name + " (sampled rows)", alibi=al)
+        # properties at full size: every output finite, causal row 0 is V[0] of its K/V head
         assert torch.isfinite(lse).all()
         assert torch.isfinite(o.float()).all()
         if w.causal:
-            assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+            G = w.H // w.kv_heads
+            assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0].repeat_interleave(G, dim=1))
 
 
 # --------------------------------------------------------------------------- #
