@@ -43,6 +43,12 @@ Readings where the pages are silent (each also listed in the design notes):
      query heads"): with Hq query heads and Hkv key/value heads (Hkv divides
      Hq), query head h reads key/value head h // (Hq / Hkv), i.e. consecutive
      query heads form the groups. Hkv = 1 is MQA, Hkv = Hq ordinary attention.
+  R10 split keys (the tiled-block guide's closing note on reducing partial
+     outputs across workers): attention restricted to a key range [kb, ke)
+     gives a partial (O_r, LSE_r) -- O_r normalised within the range, and
+     (O_r, LSE_r) = (0, -inf) for a row that sees no key there; partials of
+     disjoint ranges covering all keys merge into the full result by
+     LSE = log sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r.
   R9 ALiBi (Lesson 91 deck, slides 20-25): the logit of (i, j) in head h gains
      the bias -m_h * |i - j| before the softmax, on top of the scaled score;
      the slopes are inputs (fp32, rounded first like the scale), and
@@ -100,11 +106,12 @@ def _as_f64(x) -> np.ndarray:
 
 def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
                   n_sink: int = 0, rows=None, chunk: int = 1024, return_probs: bool = False,
-                  alibi_slopes=None):
+                  alibi_slopes=None, key_range=None):
     """Materialised attention in fp64.
 
     q: [B, Hq, S, D]; k, v: [B, Hkv, S, D] with Hkv dividing Hq (R8); any float
     dtype, upcast exactly to fp64. alibi_slopes: optional [Hq] slopes (R9).
+    key_range: optional (kb, ke) -- only keys kb <= j < ke are visible (R10).
     rows: optional 1-D array of query positions to compute (default: all).
     Returns (O [B, Hq, R, D], LSE [B, Hq, R]) in fp64, R = len(rows); with
     return_probs=True also the normalised softmax matrix P [B, Hq, R, S]
@@ -133,6 +140,8 @@ def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
     for c0 in range(0, rows.size, chunk):
         rr = rows[c0:c0 + chunk]
         keep = visible(rr, S, causal, window, n_sink)
+        if key_range is not None:
+            keep = keep & (j_idx >= key_range[0]) & (j_idx < key_range[1])
         any_visible = keep.any(axis=1)
         dist = np.abs(rr[:, None] - j_idx).astype(np.float64)
         for b in range(B):
@@ -154,6 +163,25 @@ def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
                     P[b, h, c0:c0 + rr.size] = p / l_safe[:, None]
     if return_probs:
         return O, LSE, P
+    return O, LSE
+
+
+def merge_partials(O_parts, LSE_parts):
+    """R10: merge partial results of disjoint key ranges.
+
+    O_parts: [R, ..., D] (partial outputs, each normalised within its range);
+    LSE_parts: [R, ...]. Returns (O [..., D], LSE [...]). Parts with LSE = -inf
+    contribute nothing; if every part is -inf the row is (0, -inf).
+    """
+    O_parts = np.asarray(O_parts, dtype=np.float64)
+    L = np.asarray(LSE_parts, dtype=np.float64)
+    m = L.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(L - m_safe)                      # -inf parts -> 0
+    tot = w.sum(axis=0)
+    tot_safe = np.where(tot > 0, tot, 1.0)
+    LSE = np.where(tot > 0, m_safe + np.log(tot_safe), _NEG_INF)
+    O = (w[..., None] * O_parts).sum(axis=0) / tot_safe[..., None]
     return O, LSE
 
 

@@ -364,12 +364,72 @@ def pin_alibi_zero_slopes(orc):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def pin_split_keys_merge(orc):
+    """Partials over disjoint key ranges merge back into the full result (R10),
+    including ranges that some rows (or all rows) cannot see."""
+    B, H, S, D = 1, 3, 45, 8
+    q, k, v = _qkv(B, H, S, D, 100)
+    for causal, w, ns in MASKS[:5]:
+        full_O, full_L = orc.attention_fwd(q, k, v, causal=causal, scale=0.3, window=w,
+                                           n_sink=ns)
+        for cuts in ([0, 45], [0, 20, 45], [0, 7, 8, 30, 45], [0, 0, 44, 45], [0, 16, 32, 45]):
+            parts = [orc.attention_fwd(q, k, v, causal=causal, scale=0.3, window=w, n_sink=ns,
+                                       key_range=(a, b)) for a, b in zip(cuts[:-1], cuts[1:])]
+            O, L = orc.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+            assert np.allclose(O, full_O, rtol=0, atol=1e-12), (causal, w, cuts)
+            assert np.allclose(L, full_L, rtol=0, atol=1e-12), (causal, w, cuts)
+
+
+def pin_split_partial_brute(orc):
+    """A key-range partial is brute-force attention over the visible keys of
+    the range; rows that see none of it are (0, -inf)."""
+    B, H, S, D = 1, 2, 10, 4
+    q, k, v = _qkv(B, H, S, D, 110)
+    kb, ke = 3, 7
+    O, L = orc.attention_fwd(q, k, v, causal=True, scale=0.5, key_range=(kb, ke))
+    s = float(np.float32(0.5))
+    for h in range(H):
+        for i in range(S):
+            keys = [j for j in range(kb, ke) if j <= i]
+            if not keys:
+                assert np.all(O[0, h, i] == 0) and L[0, h, i] == -np.inf
+                continue
+            sc = [s * math.fsum(q[0, h, i, d] * k[0, h, j, d] for d in range(D)) for j in keys]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            tot = math.fsum(e)
+            want = [math.fsum(e[t] * v[0, h, j, d] for t, j in enumerate(keys)) / tot
+                    for d in range(D)]
+            assert np.allclose(O[0, h, i], want, rtol=0, atol=1e-12)
+            assert math.isclose(L[0, h, i], mx + math.log(tot), rel_tol=0, abs_tol=1e-12)
+
+
+def pin_merge_identities(orc):
+    """Merging is order-free, a single part passes through, and two equal-LSE
+    parts average with LSE + log 2."""
+    rng = np.random.default_rng(120)
+    Op = rng.standard_normal((3, 5, 4))
+    Lp = rng.standard_normal((3, 5)) * 3
+    Lp[1, 2] = -np.inf
+    O, L = orc.merge_partials(Op, Lp)
+    Or, Lr = orc.merge_partials(Op[::-1], Lp[::-1])
+    assert np.allclose(O, Or, rtol=0, atol=1e-14) and np.allclose(L, Lr, rtol=0, atol=1e-14)
+    O1, L1 = orc.merge_partials(Op[:1], Lp[:1])
+    assert np.allclose(O1, Op[0], rtol=0, atol=1e-15) and np.array_equal(L1, Lp[0])
+    O2, L2 = orc.merge_partials(np.stack([Op[0], Op[2]]), np.stack([Lp[0], Lp[0]]))
+    assert np.allclose(O2, (Op[0] + Op[2]) / 2, rtol=0, atol=1e-14)
+    assert np.allclose(L2, Lp[0] + math.log(2), rtol=0, atol=1e-14)
+    Oe, Le = orc.merge_partials(np.zeros((2, 1, 3)), np.full((2, 1), -np.inf))
+    assert np.all(Oe == 0) and np.all(Le == -np.inf)
+
+
 PINS = [pin_bruteforce, pin_probs, pin_constant_v, pin_causal_row0, pin_prefix_independence,
         pin_tiled_block_invariance, pin_lab3_worked_example, pin_sdpa_library,
         pin_closed_form_scale0, pin_window_degenerate, pin_shift_invariance,
         pin_permutation_noncausal, pin_row_subset, pin_bruteforce_groups_alibi,
         pin_groups_equal_repeated_heads, pin_alibi_slope_rule, pin_alibi_closed_form,
-        pin_alibi_sdpa_library, pin_alibi_zero_slopes]
+        pin_alibi_sdpa_library, pin_alibi_zero_slopes, pin_split_keys_merge,
+        pin_split_partial_brute, pin_merge_identities]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -464,6 +524,12 @@ MUTATIONS = {
     "alibi_wrong_head": ("scores = scores - slopes[h] * dist",
                          "scores = scores - slopes[g] * dist"),
     # the deck's trap (slide 28): the bias added to the probabilities, after the softmax
+    "key_range_inclusive_end": ("(j_idx < key_range[1])", "(j_idx <= key_range[1])"),
+    "merge_without_max": ("w = np.exp(L - m_safe)", "w = np.exp(L)"),
+    "merge_plain_average": ("O = (w[..., None] * O_parts).sum(axis=0) / tot_safe[..., None]",
+                            "O = O_parts.mean(axis=0)"),
+    "merge_lse_max_only": ("LSE = np.where(tot > 0, m_safe + np.log(tot_safe), _NEG_INF)",
+                           "LSE = np.where(tot > 0, m_safe, _NEG_INF)"),
     "alibi_after_softmax": [("scores = scores - slopes[h] * dist", "pass"),
                             ("P[b, h, c0:c0 + rr.size] = p / l_safe[:, None]",
                              "P[b, h, c0:c0 + rr.size] = p / l_safe[:, None] - "
