@@ -198,9 +198,19 @@ def main():
     slopes = (torch.tensor(alibi_slopes(w.H), dtype=torch.float32, device=dev)
               if w.alibi else None)
 
+    ws = None
+    if w.n_split > 1:
+        ws = torch.empty(fa.flash_attn_split_workspace_bytes(w.B, w.H, w.S, w.D, w.n_split),
+                         dtype=torch.uint8, device=dev)
+
     def step():
-        fa.flash_attn_fwd(qd, kd, vd, causal=w.causal, window=w.window, n_sink=w.n_sink,
-                          scale=w.scale, alibi_slopes=slopes, out=o, lse=lse)
+        if w.n_split > 1:
+            fa.flash_attn_fwd_split(qd, kd, vd, n_split=w.n_split, causal=w.causal,
+                                    window=w.window, n_sink=w.n_sink, scale=w.scale,
+                                    alibi_slopes=slopes, workspace=ws, out=o, lse=lse)
+        else:
+            fa.flash_attn_fwd(qd, kd, vd, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                              scale=w.scale, alibi_slopes=slopes, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -242,7 +252,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: Q, K, V iid N(0,1), numpy default_rng(seed 0), rounded to dtype",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
-                   "alibi": w.alibi,
+                   "alibi": w.alibi, "n_split": w.n_split,
                    "causal": w.causal, "window": w.window, "n_sink": w.n_sink,
                    "scale": w.scale, "layout": "[B,H,S,D] contiguous",
                    "flops_per_step": flops, "nominal_flops_per_step": nominal_flops(w),

@@ -46,6 +46,7 @@ class Workload:
     lab3_draw: bool = False   # reproduce the Lab 3 page's (64, 16) float64 draw
     H_kv: int = 0             # key/value heads (0: same as H)
     alibi: bool = False       # ALiBi bias with the Lesson 91 deck's slopes
+    n_split: int = 1          # key ranges per query block (partials + merge)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -86,6 +87,11 @@ EXTENSIONS = {
     "alibi_causal_b4h16s4096d128_bf16": Workload(
         "alibi_causal_b4h16s4096d128_bf16", 4, 16, 4096, 128, "bf16", True,
         1.0 / math.sqrt(128), alibi=True),
+    # Few heads: 8 heads x 16 query blocks fill a sixth of the CUs; splitting
+    # the keys of each query block four ways fills them.
+    "split4_causal_b1h8s4096d128_bf16": Workload(
+        "split4_causal_b1h8s4096d128_bf16", 1, 8, 4096, 128, "bf16", True,
+        1.0 / math.sqrt(128), n_split=4),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTENSIONS}
 

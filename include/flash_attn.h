@@ -116,6 +116,63 @@ int flash_attn_fwd_ext(const void* q, const void* k, const void* v, void* o, flo
                        const float* alibi_slopes, void* stream, int dtype);
 
 /*
+ * flash_attn_fwd_split -- flash_attn_fwd_ext with the keys of every query
+ * block split into n_split ranges computed by separate work-groups, then
+ * merged. More work-groups in flight for short sequences or few heads.
+ *
+ * Each range yields a partial result (O_s normalised within the range, LSE_s;
+ * (0, -inf) for a row that sees no key of the range), and the partials merge
+ * into O and LSE by LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s
+ * (the online-softmax rescale of the Lesson 91 deck, slide 11, applied once
+ * per range; the NumPy tiled-block guide ends on reducing partial outputs
+ * across workers). The result equals flash_attn_fwd_ext's up to rounding
+ * order; O is rounded to `dtype` once, after the merge.
+ *
+ * n_split   : 1..256. 1 computes exactly flash_attn_fwd_ext (no workspace
+ *             needed). n_split > 1 needs dtype FA_BF16 / FA_F16 and D 64 or
+ *             128 (else FA_ERR_UNSUPPORTED).
+ * workspace : device memory the caller owns, >= flash_attn_split_workspace_bytes(
+ *             B, H, S, D, n_split) bytes, 16-byte aligned, overlapping no
+ *             tensor. Scratch only: its contents on entry do not matter and
+ *             are undefined afterwards. Calls that share a workspace must not
+ *             overlap in time.
+ * Everything else as flash_attn_fwd_ext, plus FA_ERR_INVALID for n_split out
+ * of range or a missing / small / misaligned / overlapping workspace. Two
+ * kernels are enqueued on `stream` (partials, then the merge).
+ */
+int flash_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D,
+                         int causal, int64_t window, int64_t n_sink, float scale,
+                         const float* alibi_slopes, int64_t n_split, void* workspace,
+                         int64_t workspace_bytes, void* stream, int dtype);
+
+/*
+ * flash_attn_split_workspace_bytes -- host-only: the workspace bytes
+ * flash_attn_fwd_split needs for this shape (0 for n_split == 1), or -1 with
+ * flash_attn_last_error() set for invalid sizes.
+ */
+int64_t flash_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D,
+                                         int64_t n_split);
+
+/*
+ * flash_attn_merge -- merge n_parts partial attention results row by row, as
+ * flash_attn_fwd_split does internally (and as a sequence-sharded pass would
+ * after computing partials on key shards).
+ *
+ * o_parts   : device, fp32 [n_parts, rows, D], 16-byte aligned (each partial
+ *             normalised within its key range).
+ * lse_parts : device, fp32 [n_parts, rows], 4-byte aligned (-inf: the part
+ *             saw no key for that row and weighs zero).
+ * o         : device, [rows, D] in `dtype`, 16-byte aligned; lse: device fp32
+ *             [rows], 4-byte aligned. A row with no finite partial becomes
+ *             (0, -inf). Outputs must not overlap the inputs or each other.
+ * n_parts in [1, 4096], rows >= 1, D in {16, 32, 64, 128} (else
+ * FA_ERR_UNSUPPORTED). Asynchronous on `stream`, like flash_attn_fwd.
+ */
+int flash_attn_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, int64_t rows,
+                     int64_t D, void* o, float* lse, void* stream, int dtype);
+
+/*
  * flash_attn_fwd_counted -- flash_attn_fwd plus an instrumentation counter.
  *
  * block_pairs : device pointer to one uint64 (8-byte aligned), or NULL. When

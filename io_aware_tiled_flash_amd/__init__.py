@@ -12,7 +12,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_tile_shape",
+__all__ = ["flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_fwd_split", "flash_attn_merge",
+           "flash_attn_split_workspace_bytes", "flash_attn_tile_shape",
            "flash_attn_last_error", "flash_attn_version", "capi", "library_path",
            "FA_F32", "FA_F16", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED",
            "FA_ERR_HIP"]
@@ -39,6 +40,14 @@ class _CAPI:
         self.flash_attn_fwd_ext = self._fn(
             "flash_attn_fwd_ext",
             [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp, vp, i32], i32)
+        self.flash_attn_fwd_split = self._fn(
+            "flash_attn_fwd_split",
+            [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp, i64, vp, i64, vp,
+             i32], i32)
+        self.flash_attn_split_workspace_bytes = self._fn(
+            "flash_attn_split_workspace_bytes", [i64, i64, i64, i64, i64], i64)
+        self.flash_attn_merge = self._fn(
+            "flash_attn_merge", [vp, vp, i64, i64, i64, vp, vp, vp, i32], i32)
         self.flash_attn_tile_shape = self._fn(
             "flash_attn_tile_shape",
             [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
@@ -99,7 +108,8 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alibi_slopes=None):
+def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alibi_slopes=None,
+             n_split=None, workspace=None):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
@@ -134,7 +144,18 @@ def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alib
         stream = torch.cuda.current_stream(q.device).cuda_stream
         ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr())
         mask = (int(bool(causal)), int(window), int(n_sink), float(scale))
-        if Hkv != H or alibi_slopes is not None:
+        if n_split is not None:
+            need = capi().flash_attn_split_workspace_bytes(B, H, S, D, int(n_split))
+            if need < 0:
+                _check(FA_ERR_INVALID)
+            if workspace is None and need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            ws_ptr = None if workspace is None else workspace.data_ptr()
+            ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+            slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+            rc = capi().flash_attn_fwd_split(*ptrs, B, H, Hkv, S, D, *mask, slopes, int(n_split),
+                                             ws_ptr, ws_bytes, stream, _dtype_code(q))
+        elif Hkv != H or alibi_slopes is not None:
             if block_pairs is not None:
                 raise ValueError("the block counter is available for plain multi-head calls only")
             slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
@@ -166,6 +187,53 @@ def flash_attn_fwd(q, k, v, *, causal: bool = False, window: int = 0, n_sink: in
     synchronisation happens here.
     """
     return _forward(q, k, v, causal, window, n_sink, scale, out, lse, None, alibi_slopes)
+
+
+def flash_attn_fwd_split(q, k, v, *, n_split: int, causal: bool = False, window: int = 0,
+                         n_sink: int = 0, scale: float | None = None, alibi_slopes=None,
+                         workspace=None, out=None, lse=None):
+    """flash_attn_fwd with the keys of every query block split into n_split
+    ranges (separate work-groups) whose partial results are then merged.
+    workspace: optional GPU tensor of at least flash_attn_split_workspace_bytes
+    bytes (allocated here through torch when None)."""
+    return _forward(q, k, v, causal, window, n_sink, scale, out, lse, None, alibi_slopes,
+                    n_split, workspace)
+
+
+def flash_attn_split_workspace_bytes(B: int, H: int, S: int, D: int, n_split: int) -> int:
+    n = capi().flash_attn_split_workspace_bytes(B, H, S, D, n_split)
+    if n < 0:
+        _check(FA_ERR_INVALID)
+    return n
+
+
+def flash_attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None):
+    """Merge partial results: o_parts fp32 [n, ..., D], lse_parts fp32 [n, ...]
+    (GPU, contiguous) -> (o [..., D] in dtype (default float32), lse [...])."""
+    import torch
+    if not (isinstance(o_parts, torch.Tensor) and isinstance(lse_parts, torch.Tensor)):
+        raise ValueError("o_parts and lse_parts must be torch tensors")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not (o_parts.is_cuda and lse_parts.is_cuda and o_parts.is_contiguous()
+            and lse_parts.is_contiguous()):
+        raise ValueError("partials must be contiguous GPU tensors")
+    if o_parts.dim() < 2 or o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts must be [n, ..., D] and lse_parts [n, ...]")
+    n, D = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    dtype = torch.float32 if dtype is None else dtype
+    o = torch.empty(o_parts.shape[1:], dtype=dtype, device=o_parts.device) if out is None else out
+    l = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device) \
+        if lse is None else lse
+    if o.shape != o_parts.shape[1:] or not o.is_contiguous() or l.shape != lse_parts.shape[1:]:
+        raise ValueError("out / lse shapes do not match the partials")
+    with torch.cuda.device(o_parts.device):
+        stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+        rc = capi().flash_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, rows, D,
+                                     o.data_ptr(), l.data_ptr(), stream, _dtype_code(o))
+    _check(rc)
+    return o, l
 
 
 def flash_attn_fwd_counted(q, k, v, block_pairs, *, causal: bool = False, window: int = 0,

@@ -40,9 +40,21 @@ int elem_bytes(int dtype) {
 
 bool supported_d(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
+// Bytes of the key-split workspace: fp32 partial outputs [n_split][B*H][S][D]
+// then, 256-byte aligned, partial LSE [n_split][B*H][S]. -1 if it overflows.
+int64_t split_ws_bytes(int64_t rows, int64_t D, int64_t n_split, int64_t* lse_offset) {
+  const int64_t lim = INT64_MAX / 8;
+  if (rows > lim / n_split || rows * n_split > lim / (D + 1)) return -1;
+  const int64_t o_bytes = rows * n_split * D * 4;
+  const int64_t off = (o_bytes + 255) / 256 * 256;
+  if (lse_offset) *lse_offset = off;
+  return off + rows * n_split * 4;
+}
+
 int forward(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
             int64_t Hkv, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
-            float scale, const float* alibi, void* stream, int dtype, uint64_t* block_pairs) {
+            float scale, const float* alibi, void* stream, int dtype, uint64_t* block_pairs,
+            int64_t n_split = 1, void* workspace = nullptr, int64_t workspace_bytes = 0) {
   g_last_error.clear();
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID, "null tensor pointer");
   if (B < 1 || H < 1 || S < 1) return fail(FA_ERR_INVALID, "B, H and S must be >= 1");
@@ -80,11 +92,29 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
                 overlaps(alibi, (uint64_t)H * 4, lse, (uint64_t)rows * 4)))
     return fail(FA_ERR_INVALID, "alibi_slopes overlaps o or lse");
 
+  if (n_split < 1 || n_split > 256) return fail(FA_ERR_INVALID, "n_split must be in [1, 256]");
+  int64_t lse_off = 0;
+  if (n_split > 1) {
+    const int64_t need = split_ws_bytes(rows, D, n_split, &lse_off);
+    if (need < 0) return fail(FA_ERR_INVALID, "workspace size overflows");
+    if (!workspace) return fail(FA_ERR_INVALID, "null workspace");
+    if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need) return fail(FA_ERR_INVALID, "workspace too small");
+    const uint64_t wb = (uint64_t)need;
+    if (overlaps(workspace, wb, q, tbytes) || overlaps(workspace, wb, k, kvbytes) ||
+        overlaps(workspace, wb, v, kvbytes) || overlaps(workspace, wb, o, tbytes) ||
+        overlaps(workspace, wb, lse, (uint64_t)rows * 4) ||
+        (alibi && overlaps(workspace, wb, alibi, (uint64_t)H * 4)))
+      return fail(FA_ERR_INVALID, "workspace overlaps a tensor");
+  }
+
   if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  if (n_split > 1 && !fa::fast_supported((int)D, dtype))
+    return fail(FA_ERR_UNSUPPORTED, "key splitting needs bf16 / f16 with head dim 64 or 128");
   const fa::Plan plan = fa::plan_fwd(B * H, S, D, dtype);
   const int64_t br = plan.block_q;
   const int64_t nqb = (S + br - 1) / br;
-  if (S > INT32_MAX - 2 * br || bh > INT32_MAX || nqb * bh > (int64_t)UINT32_MAX / 256)
+  if (S > INT32_MAX - 2 * br || bh > INT32_MAX || nqb * bh * n_split > (int64_t)INT32_MAX / 256)
     return fail(FA_ERR_UNSUPPORTED, "S, B*H or the grid exceed the 32-bit index range");
 
   fa::FwdParams p;
@@ -95,6 +125,13 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.lse = lse;
   p.block_pairs = reinterpret_cast<unsigned long long*>(block_pairs);
   p.alibi = alibi;
+  p.n_split = (int)n_split;
+  p.o_part = nullptr;
+  p.lse_part = nullptr;
+  if (n_split > 1) {
+    p.o_part = static_cast<float*>(workspace);
+    p.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+  }
   p.S = (int)S;
   p.BH = (int)bh;
   p.H = (int)H;
@@ -115,6 +152,9 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.neg = scale < 0.f ? 1 : 0;
 
   hipError_t err = fa::launch_plan(plan, p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
+  if (err == hipSuccess && n_split > 1)
+    err = fa::launch_merge(p.o_part, p.lse_part, (int)n_split, rows, (int)D, o, lse, dtype,
+                           reinterpret_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
     return FA_ERR_HIP;
@@ -176,6 +216,62 @@ int flash_attn_fwd_ext(const void* q, const void* k, const void* v, void* o, flo
                        int dtype) {
   return forward(q, k, v, o, lse, B, H, H_kv, S, D, causal, window, n_sink, scale, alibi_slopes,
                  stream, dtype, nullptr);
+}
+
+int flash_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal,
+                         int64_t window, int64_t n_sink, float scale, const float* alibi_slopes,
+                         int64_t n_split, void* workspace, int64_t workspace_bytes, void* stream,
+                         int dtype) {
+  return forward(q, k, v, o, lse, B, H, H_kv, S, D, causal, window, n_sink, scale, alibi_slopes,
+                 stream, dtype, nullptr, n_split, workspace, workspace_bytes);
+}
+
+int64_t flash_attn_split_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D,
+                                         int64_t n_split) {
+  g_last_error.clear();
+  if (B < 1 || H < 1 || S < 1 || D < 1 || n_split < 1 || n_split > 256) {
+    fail(FA_ERR_INVALID, "B, H, S, D must be >= 1 and n_split in [1, 256]");
+    return -1;
+  }
+  if (B > INT64_MAX / H || B * H > INT64_MAX / S) {
+    fail(FA_ERR_INVALID, "B*H*S overflows");
+    return -1;
+  }
+  if (n_split == 1) return 0;
+  const int64_t r = split_ws_bytes(B * H * S, D, n_split, nullptr);
+  if (r < 0) fail(FA_ERR_INVALID, "workspace size overflows");
+  return r;
+}
+
+int flash_attn_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, int64_t rows,
+                     int64_t D, void* o, float* lse, void* stream, int dtype) {
+  g_last_error.clear();
+  if (!o_parts || !lse_parts || !o || !lse) return fail(FA_ERR_INVALID, "null pointer");
+  if (n_parts < 1 || n_parts > 4096 || rows < 1 || D < 1)
+    return fail(FA_ERR_INVALID, "n_parts in [1, 4096], rows and D must be >= 1");
+  const int e = elem_bytes(dtype);
+  if (e == 0) return fail(FA_ERR_INVALID, "unknown dtype");
+  if (!aligned(o_parts, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID, "o_parts and o must be 16-byte aligned");
+  if (!aligned(lse_parts, 4) || !aligned(lse, 4))
+    return fail(FA_ERR_INVALID, "lse_parts and lse must be 4-byte aligned");
+  const int64_t lim = INT64_MAX / 8;
+  if (rows > lim / n_parts || rows * n_parts > lim / D) return fail(FA_ERR_INVALID, "size overflows");
+  const uint64_t pb = (uint64_t)(rows * n_parts * D * 4), lb = (uint64_t)(rows * n_parts * 4);
+  const uint64_t ob = (uint64_t)(rows * D * e), ol = (uint64_t)(rows * 4);
+  if (overlaps(o, ob, o_parts, pb) || overlaps(o, ob, lse_parts, lb) ||
+      overlaps(lse, ol, o_parts, pb) || overlaps(lse, ol, lse_parts, lb) || overlaps(o, ob, lse, ol))
+    return fail(FA_ERR_INVALID, "outputs overlap the partials or each other");
+  if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  if (rows > (int64_t)UINT32_MAX) return fail(FA_ERR_UNSUPPORTED, "too many rows");
+  hipError_t err = fa::launch_merge(o_parts, lse_parts, (int)n_parts, rows, (int)D, o, lse, dtype,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
 }
 
 int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,

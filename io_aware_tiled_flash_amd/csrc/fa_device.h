@@ -111,12 +111,14 @@ __device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, 
 // block of a head runs on one XCD; the heads are spread so that each XCD
 // holds a contiguous run of them, which keeps query heads that share a
 // key/value head (consecutive heads) on one XCD's L2 as well.
-__device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
-  const int id = blockIdx.x;
+__device__ __forceinline__ void wg_coords(const FwdParams& p, int id, int& qb, int& bh) {
   const int x = id % p.BH;
   const int rank = id / p.BH;
   bh = (p.BH & 7) ? x : (x & 7) * (p.BH >> 3) + (x >> 3);
   qb = p.causal ? (p.nqb - 1 - rank) : rank;
+}
+__device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
+  wg_coords(p, (int)blockIdx.x, qb, bh);
 }
 
 // ALiBi bias in the base-2 logit domain: turns raw (sign-folded) scores into

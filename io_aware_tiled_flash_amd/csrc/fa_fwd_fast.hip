@@ -291,6 +291,29 @@ struct Core {
       }
   }
 
+  // Partial result of a key split: O_r = O / l in fp32 and LSE_r into the
+  // workspace ([split][B*H][S][D] and [split][B*H][S]); a row that saw no key
+  // of this split gets (0, -inf).
+  __device__ __forceinline__ void epilogue_partial(const FwdParams& p, int split, int bh) {
+    const float l_tot = xhalf_sum((l[0] + l[1]) + (l[2] + l[3]));
+    if (i < p.S) {
+      const size_t row = ((size_t)split * p.BH + bh) * (size_t)p.S + i;
+      const bool any = l_tot > 0.f;
+      const float inv = any ? 1.f / l_tot : 0.f;
+      float* __restrict__ Op = p.o_part + row * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * h;
+          f32x4 w = {oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv,
+                     oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(Op + d) = w;
+        }
+      if (h == 0) p.lse_part[row] = any ? (mc + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+
   // O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
   __device__ __forceinline__ void epilogue(const FwdParams& p, size_t head, int bh) {
     const float l_tot = xhalf_sum((l[0] + l[1]) + (l[2] + l[3]));
@@ -340,8 +363,12 @@ void fa_fwd_fast_kernel(FwdParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
+  // With a key split, work-group id = split * (nqb * BH) + (the id of the
+  // unsplit launch); each split takes a contiguous share of the key blocks.
+  const int per = p.nqb * p.BH;
+  const int split = (int)blockIdx.x / per;
   int qb, bh;
-  wg_coords(p, qb, bh);
+  wg_coords(p, (int)blockIdx.x - split * per, qb, bh);
   const int S = p.S;
   const int q_lo = qb * BR;
   const size_t head = (size_t)bh * (size_t)S * D;
@@ -351,7 +378,11 @@ void fa_fwd_fast_kernel(FwdParams p) {
   const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
 
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
-  const int n_iter = br.count();
+  const int n_all = br.count();
+  const int it_b = (int)((int64_t)split * n_all / p.n_split);
+  const int n_iter = (int)((int64_t)(split + 1) * n_all / p.n_split) - it_b;
+  // key block of the t-th step of this work-group
+  auto kb = [&](int t) __attribute__((always_inline)) { return br.kb(it_b + t); };
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
 
   TileDma<T, D, NW, false> kdma;
@@ -359,17 +390,17 @@ void fa_fwd_fast_kernel(FwdParams p) {
   kdma.init(wave, lane);
   vdma.init(wave, lane);
 
-  // Block 0 in flight while Q is fetched.
-  kdma.load(k0s, Kh, br.kb(0) * BC, S, wave);
-  vdma.load(v0s, Vh, br.kb(0) * BC, S, wave);
-
   C core;
+  if (n_iter > 0) {
+    // Block 0 in flight while Q is fetched.
+    kdma.load(k0s, Kh, kb(0) * BC, S, wave);
+    vdma.load(v0s, Vh, kb(0) * BC, S, wave);
+  }
   core.init(p, Qh, q_lo + 32 * wave + (lane & 31), lane, bh);
-
   wait_vmem<0>();
   __syncthreads();
 
-  // Block `it` computed from buffer pair PAR while block it+1 loads into the other.
+  // Step `it` computed from buffer pair PAR while step it+1 loads into the other.
   // MASK selects the masked variant at compile time: the visiting order is
   // [partially visible blocks][fully visible blocks][partially visible
   // blocks] (sinks and the window's first blocks, the interior, the causal
@@ -382,14 +413,14 @@ void fa_fwd_fast_kernel(FwdParams p) {
     T* kn = PAR == 0 ? k1s : k0s;
     T* vn = PAR == 0 ? v1s : v0s;
     if (it + 1 < n_iter) {
-      const int k1 = br.kb(it + 1) * BC;
+      const int k1 = kb(it + 1) * BC;
       kdma.load(kn, Kh, k1, S, wave);
       vdma.load(vn, Vh, k1, S, wave);
     }
     f32x16 sacc[C::NT];
     core.qk(sacc, kc);
-    if (decltype(mask)::value) core.mask(sacc, p, br.kb(it) * BC);
-    if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, br.kb(it) * BC + 4 * core.h);
+    if (decltype(mask)::value) core.mask(sacc, p, kb(it) * BC);
+    if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, kb(it) * BC + 4 * core.h);
     typename C::v8 pb[C::NT][2];
     core.softmax(sacc, pb);
     core.pv(vc, pb);
@@ -407,15 +438,18 @@ void fa_fwd_fast_kernel(FwdParams p) {
     if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
   };
   int f0 = 0;
-  while (f0 < n_iter && !block_full<BR, BC>(q_lo, br.kb(f0) * BC, S, p.causal, p.window, p.n_sink))
+  while (f0 < n_iter && !block_full<BR, BC>(q_lo, kb(f0) * BC, S, p.causal, p.window, p.n_sink))
     ++f0;
   int f1 = f0;
-  while (f1 < n_iter && block_full<BR, BC>(q_lo, br.kb(f1) * BC, S, p.causal, p.window, p.n_sink))
+  while (f1 < n_iter && block_full<BR, BC>(q_lo, kb(f1) * BC, S, p.causal, p.window, p.n_sink))
     ++f1;
   segment(std::true_type{}, 0, f0);
   segment(std::false_type{}, f0, f1);
   segment(std::true_type{}, f1, n_iter);
-  core.epilogue(p, head, bh);
+  if (p.o_part)
+    core.epilogue_partial(p, split, bh);
+  else
+    core.epilogue(p, head, bh);
 }
 
 // ------------------------------------------------------------------------ //
@@ -444,7 +478,7 @@ FA_FAST_INST(_Float16, 64, 4)
 
 template <typename T, int D, bool ALIBI>
 static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {
-  const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH;
+  const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH * (unsigned)p.n_split;
   if (nw == 8)
     hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, ALIBI>), dim3(grid), dim3(512), 0, st, p);
   else

@@ -20,6 +20,9 @@ struct FwdParams {
   float* lse;
   unsigned long long* block_pairs;  // optional instrumentation counter (may be null)
   const float* alibi;  // per-query-head ALiBi slopes [H], or null (no bias)
+  float* o_part;       // key-split partial outputs [n_split][BH][S][D] fp32, or null
+  float* lse_part;     // key-split partial LSE [n_split][BH][S] (with o_part)
+  int n_split;         // key-block ranges per query block (1: no split)
   int S;        // sequence length
   int BH;       // batch * query heads
   int H;        // query heads
@@ -36,6 +39,11 @@ struct FwdParams {
 int generic_tile_rows();
 int generic_tile_keys();
 hipError_t launch_generic(const FwdParams& p, int D, int dtype, hipStream_t st);
+
+// Merge of key-split partials: o[r] = sum_s exp(lse_part[s][r] - lse[r]) o_part[s][r],
+// lse[r] = log sum_s exp(lse_part[s][r]); rows = number of rows r; dtype of o.
+hipError_t launch_merge(const float* o_part, const float* lse_part, int n_split, int64_t rows,
+                        int D, void* o, float* lse, int dtype, hipStream_t st);
 
 // Fast kernels: bf16 / f16 with D in {64, 128}; nw = waves per work-group (4 or 8).
 bool fast_supported(int D, int dtype);

@@ -33,7 +33,8 @@ def _declared_functions():
 
 def test_headers_declare_the_abi():
     names = _declared_functions()
-    assert {"flash_attn_fwd", "flash_attn_fwd_ext", "flash_attn_fwd_counted",
+    assert {"flash_attn_fwd", "flash_attn_fwd_ext", "flash_attn_fwd_split",
+            "flash_attn_split_workspace_bytes", "flash_attn_merge", "flash_attn_fwd_counted",
             "flash_attn_tile_shape", "flash_attn_last_error", "flash_attn_version"} <= names
 
 
@@ -168,3 +169,85 @@ def test_python_wrapper_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 8, 16)
     with pytest.raises(ValueError):
         fa.flash_attn_fwd(x, x, x)
+
+
+# --------------------------------------------------------------------------- #
+# Key splitting and the merge
+# --------------------------------------------------------------------------- #
+
+WS = 0x10000000   # fake workspace address, far from the tensors
+
+
+def _call_split(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, H_kv=2, S=64, D=64, causal=1, window=0,
+                n_sink=0, scale=0.125, alibi=None, n_split=2, ws=WS, ws_bytes=1 << 30,
+                stream=None, dtype=fa.FA_BF16):
+    rc = fa.capi().flash_attn_fwd_split(q, k, v, o, lse, B, H, H_kv, S, D, causal, window,
+                                        n_sink, scale, alibi, n_split, ws, ws_bytes, stream,
+                                        dtype)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID_SPLIT = {
+    "n_split_zero": dict(n_split=0),
+    "n_split_too_large": dict(n_split=257),
+    "null_workspace": dict(ws=None),
+    "workspace_misaligned": dict(ws=WS + 8),
+    "workspace_too_small": dict(ws_bytes=1024),
+    "workspace_overlaps_o": dict(ws=O),
+    "workspace_overlaps_q": dict(ws=Q - 4096),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID_SPLIT))
+def test_invalid_split_arguments_rejected(case):
+    rc, msg = _call_split(**INVALID_SPLIT[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+    assert msg
+
+
+def test_split_needs_fast_path():
+    for kw in (dict(dtype=fa.FA_F32), dict(D=16), dict(D=32)):
+        rc, msg = _call_split(**kw)
+        assert rc == fa.FA_ERR_UNSUPPORTED, (kw, msg)
+
+
+def test_split_workspace_bytes():
+    c = fa.capi()
+    rows, D = 2 * 8 * 1024, 64
+    n = c.flash_attn_split_workspace_bytes(2, 8, 1024, 64, 4)
+    o_bytes = 4 * rows * D * 4
+    assert n == (o_bytes + 255) // 256 * 256 + 4 * rows * 4
+    assert c.flash_attn_split_workspace_bytes(2, 8, 1024, 64, 1) == 0
+    assert c.flash_attn_split_workspace_bytes(2, 8, 1024, 64, 0) == -1
+    assert fa.flash_attn_last_error()
+    assert c.flash_attn_split_workspace_bytes(1 << 40, 1 << 20, 1 << 10, 64, 2) == -1
+
+
+def _call_merge(op=WS, lp=WS + (1 << 26), n=3, rows=100, D=64, o=O, lse=L, dtype=fa.FA_BF16):
+    rc = fa.capi().flash_attn_merge(op, lp, n, rows, D, o, lse, None, dtype)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID_MERGE = {
+    "null_parts": dict(op=None),
+    "null_lse": dict(lse=None),
+    "n_zero": dict(n=0),
+    "rows_zero": dict(rows=0),
+    "parts_misaligned": dict(op=WS + 4),
+    "o_misaligned": dict(o=O + 8),
+    "lse_misaligned": dict(lse=L + 2),
+    "o_overlaps_parts": dict(o=WS + 64),
+    "lse_overlaps_o": dict(lse=O + 16),
+    "dtype_unknown": dict(dtype=9),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID_MERGE))
+def test_invalid_merge_arguments_rejected(case):
+    rc, msg = _call_merge(**INVALID_MERGE[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+
+
+def test_merge_unsupported_head_dim():
+    rc, msg = _call_merge(D=48)
+    assert rc == fa.FA_ERR_UNSUPPORTED

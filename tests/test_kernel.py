@@ -96,8 +96,14 @@ def test_workload_parity(name):
     slopes = ORACLE.alibi_slopes(w.H).astype(np.float32) if w.alibi else None
     sd = None if slopes is None else torch.from_numpy(slopes).cuda()
     _say(f"workload {name}: launching")
-    o, lse = gpu_fwd(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink, scale=w.scale,
-                     alibi_slopes=sd)
+    if w.n_split > 1:
+        o, lse = fa.flash_attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), n_split=w.n_split,
+                                         causal=w.causal, window=w.window, n_sink=w.n_sink,
+                                         scale=w.scale, alibi_slopes=sd)
+        torch.cuda.synchronize()
+    else:
+        o, lse = gpu_fwd(q, k, v, causal=w.causal, window=w.window, n_sink=w.n_sink,
+                         scale=w.scale, alibi_slopes=sd)
     assert o.shape == q.shape and o.dtype == q.dtype and lse.shape == q.shape[:3]
     al = None if slopes is None else slopes.astype(np.float64)
     small = w.B * w.H * w.S <= 32768
@@ -364,3 +370,95 @@ def test_alibi_rejects_bad_slopes_tensor():
     with pytest.raises(ValueError):
         fa.flash_attn_fwd(q, k, v, alibi_slopes=torch.zeros(4, dtype=torch.float64,
                                                              device="cuda"))
+
+
+# --------------------------------------------------------------------------- #
+# Key-split partials and the merge
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_keys(dtype, D):
+    """flash_attn_fwd_split against the oracle for several split counts (more
+    splits than key blocks included), every mask, ragged S, grouped heads and
+    ALiBi."""
+    for S in (100, 700, 1029):
+        q, _, _ = fa_inputs.make_qkv(2, 4, S, D, dtype, seed=S + 31)
+        k, v = _kv(2, 2, S, D, dtype, seed=S + 32)
+        for n_split in (1, 2, 3, 7):
+            for causal, window, n_sink in MASKS[:3]:
+                scale = 1.0 / math.sqrt(D)
+                qd, kd, vd = (t.cuda() for t in (q, k, v))
+                o, lse = fa.flash_attn_fwd_split(qd, kd, vd, n_split=n_split, causal=causal,
+                                                 window=window, n_sink=n_sink, scale=scale)
+                torch.cuda.synchronize()
+                compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                        n_sink=n_sink, heads=[(0, 0), (1, 3)],
+                        label=f"{dtype} D{D} S{S} split{n_split} c{int(causal)} w{window}")
+    # with ALiBi
+    q, k, v = fa_inputs.make_qkv(1, 4, 500, D, dtype, seed=77)
+    sl = np.array(list(ORACLE.alibi_slopes(4)), dtype=np.float32)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = fa.flash_attn_fwd_split(qd, kd, vd, n_split=3, causal=True, scale=0.1,
+                                     alibi_slopes=torch.from_numpy(sl).cuda())
+    torch.cuda.synchronize()
+    compare(o, lse, q, k, v, dtype, causal=True, scale=0.1, alibi=sl.astype(np.float64),
+            label=f"{dtype} D{D} split3 alibi")
+
+
+def test_split_workspace_reuse_and_block_count():
+    """One caller-owned workspace serves consecutive calls of different sizes;
+    the block counter of split work-groups adds up to the unsplit count."""
+    q, k, v = (t.cuda() for t in fa_inputs.make_qkv(2, 8, 1024, 64, "f16", seed=5))
+    need = fa.flash_attn_split_workspace_bytes(2, 8, 1024, 64, 4)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # garbage contents
+    o1, l1 = fa.flash_attn_fwd_split(q, k, v, n_split=4, causal=False, scale=0.125, workspace=ws)
+    o2, l2 = fa.flash_attn_fwd(q, k, v, causal=False, scale=0.125)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2 * TOL_O["f16"]
+    assert (l1 - l2).abs().max().item() <= 1e-4
+    qs, ks, vs = (t[:, :, :300].contiguous() for t in (q, k, v))
+    o3, l3 = fa.flash_attn_fwd_split(qs, ks, vs, n_split=2, causal=True, scale=0.125, workspace=ws)
+    torch.cuda.synchronize()
+    compare(o3, l3, qs.cpu(), ks.cpu(), vs.cpu(), "f16", causal=True, scale=0.125,
+            heads=[(0, 0), (1, 7)], label="split reuse smaller")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_merge_of_oracle_partials(dtype, D):
+    """The merge kernel on partials the oracle computed (CPU, fp64 rounded to
+    fp32) against the oracle's own merge: independent of the split kernel."""
+    S, H = 90, 3
+    q, k, v = fa_inputs.make_qkv(1, H, S, D, "f32", seed=D + 1)
+    q64, k64, v64 = (fa_inputs.to_f64(t) for t in (q, k, v))
+    cuts = [0, 13, 13, 50, 90]
+    parts = [ORACLE.attention_fwd(q64, k64, v64, causal=True, scale=0.2, key_range=(a, b))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    Op = np.stack([p_[0] for p_ in parts]).astype(np.float32)     # [n, 1, H, S, D]
+    Lp = np.stack([p_[1] for p_ in parts]).astype(np.float32)     # [n, 1, H, S]
+    Om, Lm = ORACLE.merge_partials(Op.astype(np.float64), Lp.astype(np.float64))
+    o, lse = fa.flash_attn_merge(torch.from_numpy(Op).cuda(), torch.from_numpy(Lp).cuda(),
+                                 dtype=fa_inputs.DTYPES[dtype])
+    torch.cuda.synchronize()
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    # rounding: fp32 partials are exact inputs; fp32 arithmetic, then one
+    # rounding to the output type
+    tol = {"f32": 1e-5, "f16": 2e-3, "bf16": 8e-3}[dtype]
+    assert np.abs(og - Om).max() <= tol
+    assert np.abs(lg - Lm).max() <= 1e-5
+    # every row of the range [13, 13) part is -inf; row 0 sees only part 0
+    assert np.isinf(Lp[1]).all()
+
+
+def test_merge_all_parts_empty():
+    Op = torch.zeros(2, 5, 64, device="cuda")
+    Lp = torch.full((2, 5), float("-inf"), device="cuda")
+    Lp[1, 3] = 0.5
+    Op[1, 3] = 2.0
+    o, lse = fa.flash_attn_merge(Op, Lp)
+    torch.cuda.synchronize()
+    assert torch.isinf(lse[[0, 1, 2, 4]]).all() and (o[[0, 1, 2, 4]] == 0).all()
+    assert lse[3].item() == pytest.approx(0.5) and torch.allclose(o[3], torch.full((64,), 2.0,
+                                                                                  device="cuda"))
