@@ -166,6 +166,57 @@ def attention_fwd(q, k, v, *, causal: bool, scale: float, window: int = 0,
     return O, LSE
 
 
+def attention_bwd(q, k, v, dO, *, causal: bool, scale: float, window: int = 0,
+                  n_sink: int = 0, alibi_slopes=None, chunk: int = 1024):
+    """Gradients of O = softmax(Q K^T * scale + bias + mask) V by definition, fp64.
+
+    q, dO: [B, Hq, S, D]; k, v: [B, Hkv, S, D] (R8). Returns (dQ, dK, dV) in fp64
+    with the shapes of q, k, v; dK, dV of a key/value head sum over the query
+    heads that read it. With P the softmax matrix of a head (rows sum to 1 over
+    the visible keys) and dP = dO V^T:
+        dV = P^T dO,   dS = P * (dP - rowsum(P * dP)),
+        dQ = scale * dS K,   dK = scale * dS^T Q.
+    (rowsum(P * dP) = rowsum(dO * O): the derivative of a softmax row.) The
+    ALiBi bias and the mask are constants, so they only enter through P.
+    Backward by recomputation, as the Lesson 91 deck's closing note describes
+    it: nothing of the forward pass but its inputs (and LSE) is kept.
+    """
+    q, k, v, dO = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dO)
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape or dO.shape != q.shape or H % Hkv:
+        raise ValueError("q, dO: [B, H, S, D]; k, v: [B, H_kv, S, D] with H_kv dividing H")
+    s = fp32_scale(scale)
+    slopes = None if alibi_slopes is None else \
+        np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    j_idx = np.arange(S, dtype=np.int64)[None, :]
+    for c0 in range(0, S, chunk):
+        rr = np.arange(c0, min(S, c0 + chunk), dtype=np.int64)
+        keep = visible(rr, S, causal, window, n_sink)
+        dist = np.abs(rr[:, None] - j_idx).astype(np.float64)
+        for b in range(B):
+            for h in range(H):
+                g = kv_head(h, H, Hkv)
+                scores = (q[b, h, rr, :] @ k[b, g].T) * s
+                if slopes is not None:
+                    scores = scores - slopes[h] * dist
+                scores = np.where(keep, scores, _NEG_INF)
+                m = scores.max(axis=1)
+                m_safe = np.where(np.isfinite(m), m, 0.0)
+                p = np.exp(scores - m_safe[:, None])
+                l = p.sum(axis=1)
+                P = p / np.where(l > 0, l, 1.0)[:, None]            # [rows, S]
+                dP = dO[b, h, rr, :] @ v[b, g].T                     # [rows, S]
+                dS = P * (dP - (P * dP).sum(axis=1)[:, None])
+                dv[b, g] += P.T @ dO[b, h, rr, :]
+                dq[b, h, rr, :] = s * (dS @ k[b, g])
+                dk[b, g] += s * (dS.T @ q[b, h, rr, :])
+    return dq, dk, dv
+
+
 def merge_partials(O_parts, LSE_parts):
     """R10: merge partial results of disjoint key ranges.
 

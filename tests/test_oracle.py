@@ -423,13 +423,100 @@ def pin_merge_identities(orc):
     assert np.all(Oe == 0) and np.all(Le == -np.inf)
 
 
+def _loss_and_grads_torch(q, k, v, dO, causal, scale, window, n_sink, slopes=None):
+    """torch autograd (CPU, fp64) through the plain definition with an explicit
+    float mask -- a library differentiation of the same function."""
+    B, H, S, D = q.shape
+    G = H // k.shape[1]
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    kk = tk.repeat_interleave(G, dim=1)
+    vv = tv.repeat_interleave(G, dim=1)
+    keep = torch.from_numpy(ORACLE.visible(np.arange(S), S, causal, window, n_sink))
+    sc = (tq @ kk.transpose(-1, -2)) * float(np.float32(scale))
+    if slopes is not None:
+        i = torch.arange(S)[:, None]
+        j = torch.arange(S)[None, :]
+        sl = torch.tensor(np.asarray(slopes, np.float32).astype(np.float64))
+        sc = sc - sl[None, :, None, None] * (i - j).abs().double()[None, None]
+    sc = sc.masked_fill(~keep, float("-inf"))
+    out = torch.softmax(sc, dim=-1) @ vv
+    (out * torch.from_numpy(dO)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_bwd_autograd(orc):
+    """The backward against torch autograd of the definition (fp64, CPU), with
+    masks, grouped heads and ALiBi."""
+    for ci, (B, H, Hkv, S, D, sc, sl) in enumerate([(1, 2, 2, 23, 8, 0.3, None),
+                                                   (2, 4, 2, 17, 4, 0.7, None),
+                                                   (1, 4, 1, 19, 8, 0.2, True)]):
+        q = _rand((B, H, S, D), 200 + ci)
+        k = _rand((B, Hkv, S, D), 210 + ci)
+        v = _rand((B, Hkv, S, D), 220 + ci)
+        dO = _rand((B, H, S, D), 230 + ci)
+        slopes = orc.alibi_slopes(H) if sl else None
+        for causal, w, ns in MASKS[:5]:
+            got = orc.attention_bwd(q, k, v, dO, causal=causal, scale=sc, window=w, n_sink=ns,
+                                    alibi_slopes=slopes)
+            want = _loss_and_grads_torch(q, k, v, dO, causal, sc, w, ns, slopes)
+            for a, b_ in zip(got, want):
+                assert np.allclose(a, b_, rtol=0, atol=1e-11), (ci, causal, w, ns)
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of L = sum(O * dO) through the forward oracle."""
+    B, H, S, D = 1, 2, 7, 3
+    q, k, v = _qkv(B, H, S, D, 240)
+    dO = _rand((B, H, S, D), 241)
+    for causal, w, ns in [(False, 0, 0), (True, 0, 0), (True, 3, 1)]:
+        dq, dk, dv = orc.attention_bwd(q, k, v, dO, causal=causal, scale=0.6, window=w,
+                                       n_sink=ns)
+
+        def loss(qq, kk, vv):
+            O, _ = orc.attention_fwd(qq, kk, vv, causal=causal, scale=0.6, window=w, n_sink=ns)
+            return float((O * dO).sum())
+        eps = 1e-6
+        for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in [(0, 0, 0, 0), (0, 1, 3, 2), (0, 1, 6, 1), (0, 0, 5, 0)]:
+                a1, a2 = arr.copy(), arr.copy()
+                a1[idx] += eps
+                a2[idx] -= eps
+                args1 = {"qq": q, "kk": k, "vv": v}
+                args2 = dict(args1)
+                args1[name * 2], args2[name * 2] = a1, a2
+                fd = (loss(**args1) - loss(**args2)) / (2 * eps)
+                assert abs(fd - grad[idx]) < 1e-7, (name, idx, causal, fd, grad[idx])
+
+
+def pin_bwd_invariants(orc):
+    """Shifting every key of a head by one vector leaves every output unchanged,
+    so the key gradients of a head sum to zero; dO = 0 gives zero gradients;
+    dO = 1 gives dV_j = the column sums of P."""
+    B, H, S, D = 1, 2, 20, 6
+    q, k, v = _qkv(B, H, S, D, 250)
+    dO = _rand((B, H, S, D), 251)
+    for causal, w, ns in MASKS[:5]:
+        dq, dk, dv = orc.attention_bwd(q, k, v, dO, causal=causal, scale=0.5, window=w,
+                                       n_sink=ns)
+        assert np.allclose(dk.sum(axis=2), 0.0, rtol=0, atol=1e-12), (causal, w)
+        z = orc.attention_bwd(q, k, v, np.zeros_like(dO), causal=causal, scale=0.5, window=w,
+                              n_sink=ns)
+        assert all(np.all(t == 0) for t in z)
+        _, _, P = orc.attention_fwd(q, k, v, causal=causal, scale=0.5, window=w, n_sink=ns,
+                                    return_probs=True)
+        _, _, dv1 = orc.attention_bwd(q, k, v, np.ones_like(dO), causal=causal, scale=0.5,
+                                      window=w, n_sink=ns)
+        assert np.allclose(dv1, P.sum(axis=2)[..., None].repeat(D, axis=-1), rtol=0, atol=1e-12)
+
+
 PINS = [pin_bruteforce, pin_probs, pin_constant_v, pin_causal_row0, pin_prefix_independence,
         pin_tiled_block_invariance, pin_lab3_worked_example, pin_sdpa_library,
         pin_closed_form_scale0, pin_window_degenerate, pin_shift_invariance,
         pin_permutation_noncausal, pin_row_subset, pin_bruteforce_groups_alibi,
         pin_groups_equal_repeated_heads, pin_alibi_slope_rule, pin_alibi_closed_form,
         pin_alibi_sdpa_library, pin_alibi_zero_slopes, pin_split_keys_merge,
-        pin_split_partial_brute, pin_merge_identities]
+        pin_split_partial_brute, pin_merge_identities, pin_bwd_autograd,
+        pin_bwd_finite_differences, pin_bwd_invariants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -524,6 +611,10 @@ MUTATIONS = {
     "alibi_wrong_head": ("scores = scores - slopes[h] * dist",
                          "scores = scores - slopes[g] * dist"),
     # the deck's trap (slide 28): the bias added to the probabilities, after the softmax
+    "bwd_no_softmax_jacobian": ("dS = P * (dP - (P * dP).sum(axis=1)[:, None])", "dS = P * dP"),
+    "bwd_dk_unscaled": ("dk[b, g] += s * (dS.T @ q[b, h, rr, :])", "dk[b, g] += dS.T @ q[b, h, rr, :]"),
+    "bwd_dv_untransposed": ("dv[b, g] += P.T @ dO[b, h, rr, :]", "dv[b, g] += P @ dO[b, h, rr, :]"),
+    "bwd_dq_uses_v": ("dq[b, h, rr, :] = s * (dS @ k[b, g])", "dq[b, h, rr, :] = s * (dS @ v[b, g])"),
     "key_range_inclusive_end": ("(j_idx < key_range[1])", "(j_idx <= key_range[1])"),
     "merge_without_max": ("w = np.exp(L - m_safe)", "w = np.exp(L)"),
     "merge_plain_average": ("O = (w[..., None] * O_parts).sum(axis=0) / tot_safe[..., None]",
