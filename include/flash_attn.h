@@ -173,6 +173,40 @@ int flash_attn_merge(const float* o_parts, const float* lse_parts, int64_t n_par
                      int64_t D, void* o, float* lse, void* stream, int dtype);
 
 /*
+ * flash_attn_bwd -- gradients of the forward pass, by recomputation from its
+ * logsumexp (the Lesson 91 deck: the tile loop keeps only m, l and O; the
+ * backward recomputes the score tiles rather than storing them). With P the
+ * softmax weights of the forward call and dP = dout V^T:
+ *     dv = P^T dout,   dS = P * (dP - rowsum(dout * o)),
+ *     dq = scale dS K,   dk = scale dS^T Q,
+ * where a key/value head's dk, dv sum over the query heads that read it.
+ *
+ * q, o, dout, dq : device, [B, H, S, D], `dtype`, 16-byte aligned.
+ * k, v, dk, dv   : device, [B, H_kv, S, D], `dtype`, 16-byte aligned.
+ * lse            : device fp32 [B, H, S]: the lse flash_attn_fwd(_ext) wrote
+ *                  for the same inputs and arguments (o likewise).
+ * B, H, H_kv, S, D, causal, window, n_sink, scale, alibi_slopes, stream,
+ *                  dtype: as in flash_attn_fwd_ext, with dtype FA_BF16 /
+ *                  FA_F16 and D 64 or 128 (else FA_ERR_UNSUPPORTED).
+ * workspace      : device scratch of >= flash_attn_bwd_workspace_bytes(B, H, S)
+ *                  bytes (per-row rowsum(dout * o)), 16-byte aligned; contents
+ *                  on entry do not matter. Calls sharing it must not overlap.
+ * Precision: fp32 accumulation; P and dS rounded to `dtype` before their
+ * products (like P in the forward); outputs rounded once.
+ * Outputs must not overlap any input, each other or the workspace. Two
+ * kernels are enqueued on `stream`; errors as flash_attn_fwd.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
+                   float scale, const float* alibi_slopes, void* workspace,
+                   int64_t workspace_bytes, void* stream, int dtype);
+
+/* flash_attn_bwd_workspace_bytes -- host-only: bytes of flash_attn_bwd's
+ * workspace for this shape, or -1 (flash_attn_last_error set) if invalid. */
+int64_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S);
+
+/*
  * flash_attn_fwd_counted -- flash_attn_fwd plus an instrumentation counter.
  *
  * block_pairs : device pointer to one uint64 (8-byte aligned), or NULL. When

@@ -12,7 +12,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["flash_attn_fwd", "flash_attn_fwd_counted", "flash_attn_fwd_split", "flash_attn_merge",
+__all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_counted", "flash_attn_fwd_split",
+           "flash_attn_merge", "flash_attn_bwd_workspace_bytes",
            "flash_attn_split_workspace_bytes", "flash_attn_tile_shape",
            "flash_attn_last_error", "flash_attn_version", "capi", "library_path",
            "FA_F32", "FA_F16", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED",
@@ -48,6 +49,12 @@ class _CAPI:
             "flash_attn_split_workspace_bytes", [i64, i64, i64, i64, i64], i64)
         self.flash_attn_merge = self._fn(
             "flash_attn_merge", [vp, vp, i64, i64, i64, vp, vp, vp, i32], i32)
+        self.flash_attn_bwd = self._fn(
+            "flash_attn_bwd",
+            [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp,
+             vp, i64, vp, i32], i32)
+        self.flash_attn_bwd_workspace_bytes = self._fn(
+            "flash_attn_bwd_workspace_bytes", [i64, i64, i64], i64)
         self.flash_attn_tile_shape = self._fn(
             "flash_attn_tile_shape",
             [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
@@ -234,6 +241,63 @@ def flash_attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None):
                                      o.data_ptr(), l.data_ptr(), stream, _dtype_code(o))
     _check(rc)
     return o, l
+
+
+def flash_attn_bwd_workspace_bytes(B: int, H: int, S: int) -> int:
+    n = capi().flash_attn_bwd_workspace_bytes(B, H, S)
+    if n < 0:
+        _check(FA_ERR_INVALID)
+    return n
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int = 0,
+                   n_sink: int = 0, scale: float | None = None, alibi_slopes=None,
+                   workspace=None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of flash_attn_fwd on the GPU, recomputed from the
+    forward's o and lse. q, o, dout: [B, H, S, D]; k, v: [B, H_kv, S, D]; lse:
+    fp32 [B, H, S]; bf16 / f16 with D 64 or 128. workspace: optional GPU tensor
+    of at least flash_attn_bwd_workspace_bytes(B, H, S) bytes."""
+    import torch
+    ts = {"q": q, "k": k, "v": v, "o": o, "dout": dout}
+    for name, t in ts.items():
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("all tensors must share q's dtype and device")
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != (B, Hkv, S, D) \
+            or v.shape != k.shape:
+        raise ValueError("q, o, dout: [B, H, S, D]; k, v: [B, H_kv, S, D]")
+    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, S) or \
+            lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, S] on q's device")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
+                                     alibi_slopes.shape != (H,) or not alibi_slopes.is_cuda):
+        raise ValueError("alibi_slopes must be a float32 GPU tensor [H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+    need = flash_attn_bwd_workspace_bytes(B, H, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = capi().flash_attn_bwd(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
+            int(bool(causal)), int(window), int(n_sink), float(scale),
+            None if alibi_slopes is None else alibi_slopes.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), stream, _dtype_code(q))
+    _check(rc)
+    return dq, dk, dv
 
 
 def flash_attn_fwd_counted(q, k, v, block_pairs, *, causal: bool = False, window: int = 0,

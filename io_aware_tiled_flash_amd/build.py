@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflashattn.so")
 SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_fwd_fast.hip"),
-           os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_api.cpp")]
+           os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_bwd.hip"),
+           os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
 

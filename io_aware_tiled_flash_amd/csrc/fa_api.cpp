@@ -274,6 +274,102 @@ int flash_attn_merge(const float* o_parts, const float* lse_parts, int64_t n_par
   return FA_OK;
 }
 
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t S, int64_t D, int causal, int64_t window, int64_t n_sink,
+                   float scale, const float* alibi_slopes, void* workspace,
+                   int64_t workspace_bytes, void* stream, int dtype) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(FA_ERR_INVALID, "null pointer");
+  if (B < 1 || H < 1 || S < 1 || D < 1) return fail(FA_ERR_INVALID, "B, H, S and D must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(FA_ERR_INVALID, "key/value heads must be >= 1 and divide the query heads");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID, "causal must be 0 or 1");
+  if (window < 0) return fail(FA_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && !causal) return fail(FA_ERR_INVALID, "a sliding window needs causal = 1");
+  if (n_sink < 0) return fail(FA_ERR_INVALID, "n_sink must be >= 0");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "scale must be finite");
+  const int e = elem_bytes(dtype);
+  if (e == 0) return fail(FA_ERR_INVALID, "unknown dtype");
+  const void* al16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  for (const void* ptr : al16)
+    if (!aligned(ptr, 16)) return fail(FA_ERR_INVALID, "tensors and workspace must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(FA_ERR_INVALID, "lse must be 4-byte aligned");
+  if (alibi_slopes && !aligned(alibi_slopes, 4))
+    return fail(FA_ERR_INVALID, "alibi_slopes must be 4-byte aligned");
+  const int64_t lim = INT64_MAX / 8;
+  if (B > lim / H || B * H > lim / S || B * H * S > lim / D / e)
+    return fail(FA_ERR_INVALID, "tensor size overflows");
+  const int64_t rows = B * H * S;
+  const uint64_t tb = (uint64_t)(rows * D * e), kvb = tb / (uint64_t)(H / H_kv);
+  const uint64_t lb = (uint64_t)rows * 4;
+  const int64_t need = (rows * 4 + 255) / 256 * 256;
+  if (workspace_bytes < need) return fail(FA_ERR_INVALID, "workspace too small");
+  struct Region { const void* p; uint64_t n; };
+  const Region outs[] = {{dq, tb}, {dk, kvb}, {dv, kvb}, {workspace, (uint64_t)need}};
+  const Region ins[] = {{q, tb}, {k, kvb}, {v, kvb}, {o, tb}, {dout, tb}, {lse, lb},
+                        {alibi_slopes, alibi_slopes ? (uint64_t)H * 4 : 0}};
+  for (const Region& a : outs) {
+    for (const Region& b : ins)
+      if (b.p && overlaps(a.p, a.n, b.p, b.n))
+        return fail(FA_ERR_INVALID, "an output or the workspace overlaps an input");
+    for (const Region& b : outs)
+      if (&a != &b && overlaps(a.p, a.n, b.p, b.n))
+        return fail(FA_ERR_INVALID, "outputs overlap each other or the workspace");
+  }
+  if (!supported_d(D)) return fail(FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  if (!fa::bwd_supported((int)D, dtype))
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass needs bf16 / f16 with head dim 64 or 128");
+  const int64_t br = fa::bwd_tile_rows();
+  const int64_t nb = (S + br - 1) / br;
+  if (S > INT32_MAX - 2 * br || B * H > INT32_MAX || nb * B * H > (int64_t)INT32_MAX / 256)
+    return fail(FA_ERR_UNSUPPORTED, "S, B*H or the grid exceed the 32-bit index range");
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  p.alibi = alibi_slopes;
+  p.S = (int)S;
+  p.BH = (int)(B * H);
+  p.H = (int)H;
+  p.G = (int)(H / H_kv);
+  p.nqb = (int)nb;
+  p.nkb = (int)nb;
+  p.causal = causal;
+  p.window = (window >= S) ? 0 : (int)window;
+  p.n_sink = (p.window == 0) ? 0 : (int)(n_sink < S ? n_sink : S);
+  p.scale = scale;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  hipError_t err = fa::launch_bwd(p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(err);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+int64_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
+  g_last_error.clear();
+  if (B < 1 || H < 1 || S < 1) {
+    fail(FA_ERR_INVALID, "B, H and S must be >= 1");
+    return -1;
+  }
+  if (B > INT64_MAX / 8 / H || B * H > INT64_MAX / 8 / S) {
+    fail(FA_ERR_INVALID, "B*H*S overflows");
+    return -1;
+  }
+  return (B * H * S * 4 + 255) / 256 * 256;
+}
+
 int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,
                            int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t window,
                            int64_t n_sink, float scale, void* stream, int dtype,

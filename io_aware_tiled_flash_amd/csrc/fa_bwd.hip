@@ -1,0 +1,454 @@
+// Backward pass of the tiled attention for gfx950 (bf16 / f16, head dim 64
+// or 128): dQ, dK, dV by recomputation from the forward's logsumexp, without
+// storing the S x S probability matrix (the Lesson 91 deck, slide 12 and its
+// closing note: the tile loop keeps only m, l and O, and the backward
+// recomputes the tiles; the gradients themselves are those of ordinary
+// attention). With P = exp(scale Q K^T + bias - LSE) on the visible pairs,
+// dP = dO V^T and delta_i = sum_d dO_id O_id (= sum_j P_ij dP_ij):
+//     dV = P^T dO,   dS = P * (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Two kernels, both on v_mfma_f32_32x32x16 for every product:
+//  * dq kernel: one work-group per (query block of 32 * NW rows, query head).
+//    Each wave holds 32 rows of Q and dO in registers, computes its rows'
+//    delta (written to the workspace for the second kernel) and streams the
+//    visible key blocks: S^T = K Q^T and dP^T = V dO^T (K, V rows read from
+//    LDS), P and dS in registers, dQ^T += K^T dS^T with K^T read from LDS by
+//    transposing reads.
+//  * dkv kernel: one work-group per (key block of 32 * NW keys, key/value
+//    head). Each wave holds 32 keys of K and V in registers and accumulates
+//    dK^T and dV^T over the query heads of its group and the query blocks
+//    that see its keys: S = Q K^T and dP = dO V^T (Q, dO rows from LDS), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+// Tiles are staged HBM -> LDS with direct-to-LDS buffer loads in the K layout
+// of the forward kernel (16-byte chunks XOR-swizzled by row), which serves
+// both the row reads and the transposing reads without bank conflicts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_kernel.h"
+#include "fa_lds.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+
+// Per-lane element offsets of the transposing reads of a tile in the K
+// layout, relative to a 16-row chunk: lane 32h + 16grp + r16 fetches 4
+// elements of row 4h + (r16 >> 2) (lo) or that + 8 (hi), columns
+// 32 dt + 16 grp + 4 (r16 & 3) .., so that lane m of each half receives
+// column 32 dt + (m & 31) of rows {4h .. 4h+3} and {8 + 4h .. 8 + 4h+3} --
+// the k-slot order in which the C layout of a 32x32 MFMA holds its rows.
+template <int D>
+struct TrOffsets {
+  static constexpr int NDT = D / 32;
+  int lo[NDT], hi[NDT];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, grp = (lane >> 4) & 1, r16 = lane & 15;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const int row = 4 * h + (r16 >> 2) + 8 * part;
+      const int sw = k_swz<D>(row);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int chunk = 4 * dt + 2 * grp + ((r16 & 3) >> 1);
+        const int off = row * D + ((chunk ^ sw) << 3) + 4 * (r16 & 1);
+        if (part == 0)
+          lo[dt] = off;
+        else
+          hi[dt] = off;
+      }
+    }
+  }
+};
+
+// Row-read offsets (the A operand of an MFMA over d): lane (col, h) reads 8
+// elements of row col of a 32-row tile, columns 16 s + 8 h .. +7.
+template <int D>
+struct RowOffsets {
+  static constexpr int NS = D / 16;
+  int off[NS];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, col = lane & 31;
+    const int sw = k_swz<D>(col);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) off[s] = col * D + (((2 * s + h) ^ sw) << 3);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ typename Half16<T>::v8 lds_row8(const T* p) {
+  return __builtin_bit_cast(typename Half16<T>::v8, *reinterpret_cast<const u32x4*>(p));
+}
+
+template <typename T>
+__device__ __forceinline__ typename Half16<T>::v8 lds_tr8(const T* lo, const T* hi) {
+  const u32x2 a = lds_tr_read(lo);
+  const u32x2 b = lds_tr_read(hi);
+  const u32x4 w = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(typename Half16<T>::v8, w);
+}
+
+// 8 elements of a global row (16-byte aligned) as an MFMA operand; zeros
+// when the row is past the end.
+template <typename T>
+__device__ __forceinline__ typename Half16<T>::v8 load_frag(const T* __restrict__ base, int row,
+                                                            int S, int D, int d0) {
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if (row < S) w = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + d0);
+  return __builtin_bit_cast(typename Half16<T>::v8, w);
+}
+
+// Pack 8 accumulator values (k-slots of one 16-row chunk) into a B operand.
+template <typename T>
+__device__ __forceinline__ typename Half16<T>::v8 pack8(const f32x16& acc, int u) {
+  u32x4 w;
+  w[0] = pack2<T>(acc[8 * u + 0], acc[8 * u + 1]);
+  w[1] = pack2<T>(acc[8 * u + 2], acc[8 * u + 3]);
+  w[2] = pack2<T>(acc[8 * u + 4], acc[8 * u + 5]);
+  w[3] = pack2<T>(acc[8 * u + 6], acc[8 * u + 7]);
+  return __builtin_bit_cast(typename Half16<T>::v8, w);
+}
+
+// Store a 32x32 accumulator tile of X^T (rows d, columns = this lane's row r
+// of X) as X[r][32 dt + 8 g + 4 h + 0..3], multiplied by f.
+template <typename T, int D>
+__device__ __forceinline__ void store_rowT(T* __restrict__ dst, const f32x16 (&acc)[D / 32],
+                                           int h, float f) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack2<T>(acc[dt][4 * g + 0] * f, acc[dt][4 * g + 1] * f);
+      w[1] = pack2<T>(acc[dt][4 * g + 2] * f, acc[dt][4 * g + 3] * f);
+      *reinterpret_cast<u32x2*>(dst + 32 * dt + 8 * g + 4 * h) = w;
+    }
+}
+
+// Query-block range [first, last] whose rows see some key of [k_lo, k_hi].
+__device__ __forceinline__ void query_range(const BwdParams& p, int k_lo, int k_hi, int BQ,
+                                            int& first, int& last) {
+  const int nqb = (p.S + BQ - 1) / BQ;
+  first = 0;
+  last = nqb - 1;
+  if (p.causal) {
+    first = k_lo / BQ;
+    if (p.window > 0 && k_lo >= p.n_sink) {
+      const int last_row = min(p.S - 1, k_hi + p.window - 1);
+      last = last_row / BQ;
+    }
+  }
+}
+
+__device__ __forceinline__ bool visible_ij(const BwdParams& p, int i, int j) {
+  const bool in_range = (i < p.S) & (j < p.S);
+  const bool in_window = (p.window == 0) | ((i - j) < p.window) | (j < p.n_sink);
+  return in_range & ((p.causal == 0) | ((j <= i) & in_window));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------ //
+// dq kernel
+// ------------------------------------------------------------------------ //
+template <typename T, int D, bool ALIBI>
+__global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = kBwdWaves;
+  constexpr int BR = 32 * NW;
+  constexpr int BC = kBCf;
+  constexpr int NT = BC / 32;
+  constexpr int NS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE = BC * D;
+  using Tr = Half16<T>;
+  using v8 = typename Tr::v8;
+
+  __shared__ __attribute__((aligned(1024))) T ks[TILE];
+  __shared__ __attribute__((aligned(1024))) T vs[TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int bh = (int)blockIdx.x % p.BH;
+  const int rank = (int)blockIdx.x / p.BH;
+  const int qb = p.causal ? (p.nqb - 1 - rank) : rank;
+  const int S = p.S;
+  const int q_lo = qb * BR;
+  const int i = q_lo + 32 * wave + col;
+  const size_t head = (size_t)bh * S * D;
+  const size_t kv_head = (size_t)(bh / p.G) * S * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
+  const T* __restrict__ Oh = reinterpret_cast<const T*>(p.o) + head;
+  const T* __restrict__ dOh = reinterpret_cast<const T*>(p.dout) + head;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
+
+  // Q and dO rows as B operands; delta_i = dO_i . O_i
+  v8 qf[NS], df[NS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = load_frag<T>(Qh, i, S, D, 16 * s + 8 * h);
+    df[s] = load_frag<T>(dOh, i, S, D, 16 * s + 8 * h);
+    const v8 of = load_frag<T>(Oh, i, S, D, 16 * s + 8 * h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)df[s][e], (float)of[e], dpart);
+  }
+  const float delta = xhalf_sum(dpart);
+  const float lse2 = (i < S) ? p.lse[(size_t)bh * S + i] * kLog2e : 0.f;
+  if (h == 0 && i < S) p.delta[(size_t)bh * S + i] = delta;
+  const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
+
+  RowOffsets<D> ro;
+  ro.init(lane);
+  TrOffsets<D> tro;
+  tro.init(lane);
+  TileDma<T, D, NW, false> dma;
+  dma.init(wave, lane);
+
+  f32x16 dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
+  const int n_iter = br.count();
+  for (int it = 0; it < n_iter; ++it) {
+    const int k0 = br.kb(it) * BC;
+    dma.load(ks, Kh, k0, S, wave);
+    dma.load(vs, Vh, k0, S, wave);
+    wait_vmem<0>();
+    __syncthreads();
+
+    f32x16 sT[NT], pT[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sT[t][r] = 0.f;
+        pT[t][r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sT[t] = Tr::mma(lds_row8(ks + 32 * t * D + ro.off[s]), qf[s], sT[t]);
+        pT[t] = Tr::mma(lds_row8(vs + 32 * t * D + ro.off[s]), df[s], pT[t]);
+      }
+    }
+    const bool full = block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
+    v8 dsb[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        float x = p.c * sT[t][r] - lse2;
+        if (ALIBI) x -= b2 * fabsf((float)(i - j));
+        float pr = fast_exp2(x);
+        if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
+        sT[t][r] = pr * (pT[t][r] - delta);   // dS^T
+      }
+      dsb[t][0] = pack8<T>(sT[t], 0);
+      dsb[t][1] = pack8<T>(sT[t], 1);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const T* kk = ks + (32 * t + 16 * u) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          dq[dt] = Tr::mma(lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]), dsb[t][u], dq[dt]);
+      }
+    __syncthreads();
+  }
+  if (i < S) store_rowT<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)i * D, dq, h, p.scale);
+}
+
+// ------------------------------------------------------------------------ //
+// dkv kernel
+// ------------------------------------------------------------------------ //
+template <typename T, int D, bool ALIBI>
+__global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkv_kernel(BwdParams p) {
+  constexpr int NW = kBwdWaves;
+  constexpr int BK = 32 * NW;    // keys per work-group
+  constexpr int BQ = kBCf;       // query rows per streamed block
+  constexpr int NT = BQ / 32;
+  constexpr int NS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE = BQ * D;
+  using Tr = Half16<T>;
+  using v8 = typename Tr::v8;
+
+  __shared__ __attribute__((aligned(1024))) T qs[TILE];
+  __shared__ __attribute__((aligned(1024))) T dos[TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int BHkv = p.BH / p.G;
+  const int bkv = (int)blockIdx.x % BHkv;
+  const int kb = (int)blockIdx.x / BHkv;
+  const int S = p.S;
+  const int k_lo = kb * BK;
+  const int j = k_lo + 32 * wave + col;   // this lane's key
+  const size_t kv_head = (size_t)bkv * S * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
+
+  v8 kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = load_frag<T>(Kh, j, S, D, 16 * s + 8 * h);
+    vf[s] = load_frag<T>(Vh, j, S, D, 16 * s + 8 * h);
+  }
+
+  RowOffsets<D> ro;
+  ro.init(lane);
+  TrOffsets<D> tro;
+  tro.init(lane);
+  TileDma<T, D, NW, false> dma;
+  dma.init(wave, lane);
+
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+
+  int qfirst, qlast;
+  query_range(p, k_lo, min(k_lo + BK, S) - 1, BQ, qfirst, qlast);
+
+  for (int gi = 0; gi < p.G; ++gi) {
+    const int bh = bkv * p.G + gi;   // query head (b * H + h)
+    const size_t head = (size_t)bh * S * D;
+    const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
+    const T* __restrict__ dOh = reinterpret_cast<const T*>(p.dout) + head;
+    const float* __restrict__ lse = p.lse + (size_t)bh * S;
+    const float* __restrict__ dl = p.delta + (size_t)bh * S;
+    const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
+    for (int qb = qfirst; qb <= qlast; ++qb) {
+      const int q0 = qb * BQ;
+      dma.load(qs, Qh, q0, S, wave);
+      dma.load(dos, dOh, q0, S, wave);
+      // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3)
+      f32x4 l2[NT][4], dd[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = q0 + 32 * t + 8 * g + 4 * h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = r0 + e < S;
+            l2[t][g][e] = ok ? lse[r0 + e] * kLog2e : __builtin_inff();
+            dd[t][g][e] = ok ? dl[r0 + e] : 0.f;
+          }
+        }
+      wait_vmem<0>();
+      __syncthreads();
+
+      // the whole (block, key block) visible?
+      bool full = (q0 + BQ <= S) && (k_lo + BK <= S);
+      if (p.causal) {
+        full = full && (q0 >= k_lo + BK - 1);
+        if (p.window > 0)
+          full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x16 sc, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[r] = 0.f;
+          dp[r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          sc = Tr::mma(lds_row8(qs + 32 * t * D + ro.off[s]), kf[s], sc);
+          dp = Tr::mma(lds_row8(dos + 32 * t * D + ro.off[s]), vf[s], dp);
+        }
+        // rows i = q0 + 32 t + 8 g + 4 h + e, key j
+        f32x16 pm, ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int g = r >> 2, e = r & 3;
+          const int i = q0 + 32 * t + 8 * g + 4 * h + e;
+          float x = p.c * sc[r] - l2[t][g][e];
+          if (ALIBI) x -= b2 * fabsf((float)(i - j));
+          float pr = fast_exp2(x);
+          if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
+          pm[r] = pr;
+          ds[r] = pr * (dp[r] - dd[t][g][e]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const v8 pb = pack8<T>(pm, u);
+          const v8 db = pack8<T>(ds, u);
+          const T* qq = qs + (32 * t + 16 * u) * D;
+          const T* oo = dos + (32 * t + 16 * u) * D;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            dv[dt] = Tr::mma(lds_tr8(oo + tro.lo[dt], oo + tro.hi[dt]), pb, dv[dt]);
+            dk[dt] = Tr::mma(lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]), db, dk[dt]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (j < S) {
+    store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
+    store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);
+  }
+}
+
+#define FA_BWD_INST(T, D)                                                \
+  template __global__ void fa_bwd_dq_kernel<T, D, false>(BwdParams);     \
+  template __global__ void fa_bwd_dq_kernel<T, D, true>(BwdParams);      \
+  template __global__ void fa_bwd_dkv_kernel<T, D, false>(BwdParams);    \
+  template __global__ void fa_bwd_dkv_kernel<T, D, true>(BwdParams);
+FA_BWD_INST(__bf16, 128)
+FA_BWD_INST(__bf16, 64)
+FA_BWD_INST(_Float16, 128)
+FA_BWD_INST(_Float16, 64)
+#undef FA_BWD_INST
+
+bool bwd_supported(int D, int dtype) {
+  return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
+}
+int bwd_tile_rows() { return 32 * kBwdWaves; }
+
+template <typename T, int D, bool ALIBI>
+static hipError_t launch_bwd_a(const BwdParams& p, hipStream_t st) {
+  const unsigned g1 = (unsigned)p.nqb * (unsigned)p.BH;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, ALIBI>), dim3(g1), dim3(64 * kBwdWaves), 0, st, p);
+  const unsigned g2 = (unsigned)p.nkb * (unsigned)(p.BH / p.G);
+  hipLaunchKernelGGL((fa_bwd_dkv_kernel<T, D, ALIBI>), dim3(g2), dim3(64 * kBwdWaves), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
+  return p.alibi ? launch_bwd_a<T, D, true>(p, st) : launch_bwd_a<T, D, false>(p, st);
+}
+
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t st) {
+  if (dtype == kDtypeBF16) {
+    if (D == 128) return launch_bwd_t<__bf16, 128>(p, st);
+    if (D == 64) return launch_bwd_t<__bf16, 64>(p, st);
+  } else if (dtype == kDtypeF16) {
+    if (D == 128) return launch_bwd_t<_Float16, 128>(p, st);
+    if (D == 64) return launch_bwd_t<_Float16, 64>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -35,6 +35,31 @@ struct FwdParams {
   int neg;      // scale < 0
 };
 
+// Arguments of one backward launch (validated on the host). c = scale * log2(e)
+// keeps the sign of scale here: the backward kernels use the logits directly.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // forward logsumexp [BH][S]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // workspace: rowsum(dO * O) [BH][S]
+  const float* alibi;  // per-query-head slopes [H], or null
+  int S, BH, H, G;     // G = query heads per key/value head
+  int nqb, nkb;        // query blocks of the dq kernel, key blocks of the dkv kernel
+  int causal, window, n_sink;
+  float c, scale;
+};
+
+// Backward kernels: bf16 / f16 with D in {64, 128}.
+bool bwd_supported(int D, int dtype);
+int bwd_tile_rows();
+hipError_t launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t st);
+
 // Generic kernels: every dtype, D in {16, 32, 64, 128}.
 int generic_tile_rows();
 int generic_tile_keys();

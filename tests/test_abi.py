@@ -33,7 +33,8 @@ def _declared_functions():
 
 def test_headers_declare_the_abi():
     names = _declared_functions()
-    assert {"flash_attn_fwd", "flash_attn_fwd_ext", "flash_attn_fwd_split",
+    assert {"flash_attn_fwd", "flash_attn_fwd_ext", "flash_attn_fwd_split", "flash_attn_bwd",
+            "flash_attn_bwd_workspace_bytes",
             "flash_attn_split_workspace_bytes", "flash_attn_merge", "flash_attn_fwd_counted",
             "flash_attn_tile_shape", "flash_attn_last_error", "flash_attn_version"} <= names
 
@@ -251,3 +252,52 @@ def test_invalid_merge_arguments_rejected(case):
 def test_merge_unsupported_head_dim():
     rc, msg = _call_merge(D=48)
     assert rc == fa.FA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- #
+# Backward
+# --------------------------------------------------------------------------- #
+
+DO, DQ, DK, DV, BWS = 0x700000, 0x800000, 0x900000, 0xA00000, 0xB00000
+
+
+def _call_bwd(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, H_kv=2, S=64,
+              D=64, causal=1, window=0, n_sink=0, scale=0.125, alibi=None, ws=BWS,
+              ws_bytes=1 << 20, dtype=fa.FA_BF16):
+    rc = fa.capi().flash_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, S, D, causal,
+                                  window, n_sink, scale, alibi, ws, ws_bytes, None, dtype)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID_BWD = {
+    "null_dout": dict(dout=None),
+    "null_dk": dict(dk=None),
+    "null_workspace": dict(ws=None),
+    "workspace_small": dict(ws_bytes=16),
+    "dq_misaligned": dict(dq=DQ + 8),
+    "dk_overlaps_q": dict(dk=Q + 1024),
+    "dv_overlaps_dk": dict(dv=DK + 64),
+    "workspace_overlaps_dq": dict(ws=DQ),
+    "kv_heads_not_dividing": dict(H=3, H_kv=2),
+    "window_without_causal": dict(causal=0, window=4),
+    "scale_nan": dict(scale=float("nan")),
+    "dtype_unknown": dict(dtype=5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID_BWD))
+def test_invalid_bwd_arguments_rejected(case):
+    rc, msg = _call_bwd(**INVALID_BWD[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+    assert msg
+
+
+def test_bwd_unsupported_types():
+    for kw in (dict(dtype=fa.FA_F32), dict(D=32), dict(D=96)):
+        rc, msg = _call_bwd(**kw)
+        assert rc == fa.FA_ERR_UNSUPPORTED, (kw, msg)
+
+
+def test_bwd_workspace_bytes():
+    assert fa.capi().flash_attn_bwd_workspace_bytes(2, 3, 100) == (2 * 3 * 100 * 4 + 255) // 256 * 256
+    assert fa.capi().flash_attn_bwd_workspace_bytes(0, 3, 100) == -1

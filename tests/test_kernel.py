@@ -462,3 +462,88 @@ def test_merge_all_parts_empty():
     assert torch.isinf(lse[[0, 1, 2, 4]]).all() and (o[[0, 1, 2, 4]] == 0).all()
     assert lse[3].item() == pytest.approx(0.5) and torch.allclose(o[3], torch.full((64,), 2.0,
                                                                                   device="cuda"))
+
+
+# --------------------------------------------------------------------------- #
+# Backward
+# --------------------------------------------------------------------------- #
+
+# Gradient bars, normwise: max |d - d_ref| <= TOL_G * max(1, max |d_ref|) per
+# tensor. P and dS are rounded to the input type (8- or 11-bit significand,
+# relative 2^-9 / 2^-12) before the products; with fp32 accumulation over at
+# most S terms of mixed sign, the error stays a few of those units of the
+# tensor's scale, and the bars leave a factor of ~4 over 2^-9 / 2^-12 * 10.
+TOL_G = {"bf16": 2.5e-2, "f16": 4e-3}
+
+
+def _grad_err(got, ref):
+    ref = np.asarray(ref)
+    return float(np.abs(got.float().cpu().double().numpy() - ref).max() /
+                 max(1.0, float(np.abs(ref).max())))
+
+
+def _bwd_case(B, H, Hkv, S, D, dtype, causal, window, n_sink, scale, seed, slopes=None,
+              heads=None, label=""):
+    q, _, _ = fa_inputs.make_qkv(B, H, S, D, dtype, seed=seed)
+    k, v = _kv(B, Hkv, S, D, dtype, seed=seed + 1)
+    dout, _, _ = fa_inputs.make_qkv(B, H, S, D, dtype, seed=seed + 2)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, dout))
+    sd = None if slopes is None else torch.from_numpy(np.asarray(slopes, np.float32)).cuda()
+    o, lse = fa.flash_attn_fwd(qd, kd, vd, causal=causal, window=window, n_sink=n_sink,
+                               scale=scale, alibi_slopes=sd)
+    dq, dk, dv = fa.flash_attn_bwd(qd, kd, vd, o, lse, dod, causal=causal, window=window,
+                                   n_sink=n_sink, scale=scale, alibi_slopes=sd)
+    torch.cuda.synchronize()
+    rq, rk, rv = ORACLE.attention_bwd(fa_inputs.to_f64(q), fa_inputs.to_f64(k),
+                                      fa_inputs.to_f64(v), fa_inputs.to_f64(dout), causal=causal,
+                                      scale=scale, window=window, n_sink=n_sink,
+                                      alibi_slopes=slopes)
+    eq, ek, ev = _grad_err(dq, rq), _grad_err(dk, rk), _grad_err(dv, rv)
+    _say(f"  {label}: dq {eq:.2e} dk {ek:.2e} dv {ev:.2e} (tol {TOL_G[dtype]:g})")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(t.float()).all(), (label, name)
+    assert max(eq, ek, ev) <= TOL_G[dtype], (label, eq, ek, ev)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward(dtype, D):
+    for S in (1, 63, 200, 333):
+        for causal, window, n_sink in MASKS[:4]:
+            _bwd_case(1, 2, 2, S, D, dtype, causal, window, n_sink, 1.0 / math.sqrt(D),
+                      seed=S + D, label=f"{dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_grouped_heads_alibi_scale(dtype):
+    """Grouped K/V heads (dk, dv sum over the group), ALiBi, negative and zero
+    scale."""
+    _bwd_case(2, 4, 2, 257, 128, dtype, True, 0, 0, 0.088, seed=3, label="gqa")
+    _bwd_case(1, 4, 1, 190, 64, dtype, False, 0, 0, 0.125, seed=4, label="mqa")
+    _bwd_case(1, 4, 2, 230, 128, dtype, True, 0, 0, 0.088, seed=5,
+              slopes=ORACLE.alibi_slopes(4), label="alibi")
+    _bwd_case(1, 2, 2, 150, 64, dtype, True, 0, 0, -0.2, seed=6, label="negative scale")
+    _bwd_case(1, 2, 2, 150, 64, dtype, False, 0, 0, 0.0, seed=7, label="zero scale")
+
+
+def test_backward_headline_shape_sampled():
+    """The headline shape (B4 H16 S4096 D128 bf16 causal): two heads against
+    the oracle, the rest finite."""
+    B, H, S, D = 4, 16, 4096, 128
+    q, k, v = fa_inputs.make_qkv(B, H, S, D, "bf16", seed=0)
+    dout, _, _ = fa_inputs.make_qkv(B, H, S, D, "bf16", seed=9)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, dout))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.flash_attn_fwd(qd, kd, vd, causal=True, scale=scale)
+    dq, dk, dv = fa.flash_attn_bwd(qd, kd, vd, o, lse, dod, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    for b, h in [(0, 0), (3, 15)]:
+        rq, rk, rv = ORACLE.attention_bwd(
+            fa_inputs.to_f64(q[b:b + 1, h:h + 1]), fa_inputs.to_f64(k[b:b + 1, h:h + 1]),
+            fa_inputs.to_f64(v[b:b + 1, h:h + 1]), fa_inputs.to_f64(dout[b:b + 1, h:h + 1]),
+            causal=True, scale=scale)
+        errs = [_grad_err(g[b:b + 1, h:h + 1], r) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
+        _say(f"  headline head ({b},{h}): dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+        assert max(errs) <= TOL_G["bf16"]
