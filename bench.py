@@ -88,6 +88,8 @@ def copy_probe(mib: int, steps: int):
 
 
 def kernel_name(fa, w) -> str:
+    if w.backward:
+        return f"fa::fa_bwd_dq_kernel + fa::fa_bwd_dkv_kernel <{w.dtype},D={w.D}> (128-row / 128-key tiles)"
     code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w.dtype]
     bq, bk = fa.flash_attn_tile_shape(w.B, w.H, w.S, w.D, code)
     if w.dtype != "f32" and w.D in (64, 128):
@@ -99,6 +101,13 @@ def nominal_flops(w) -> float:
     """4*B*H*S^2*D, halved under the causal mask."""
     f = 4.0 * w.B * w.H * w.S * w.S * w.D
     return f / 2.0 if w.causal else f
+
+
+def work_flops(w) -> float:
+    """FLOPs of one step: the forward's algorithmic FLOPs, or for a backward
+    workload 2.5 times them (five S x S x D products -- S, dP, dV, dQ, dK --
+    against the forward's two)."""
+    return algorithmic_flops(w) * (2.5 if w.backward else 1.0)
 
 
 def algorithmic_flops(w) -> float:
@@ -142,6 +151,7 @@ def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
 
     G = w.H // w.kv_heads
     slopes = alibi_slopes(w.H) if w.alibi else None
+    dout = fa_inputs.make_dout(w) if w.backward else None
 
     def head(b, h):
         g = h // G
@@ -150,9 +160,15 @@ def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
 
     def run(arrs):
         t0 = time.perf_counter()
-        for qq, kk, vv, sl in arrs:
-            oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale, window=w.window,
-                                 n_sink=w.n_sink, alibi_slopes=sl)
+        for n_, (qq, kk, vv, sl) in enumerate(arrs):
+            if w.backward:
+                b, h = all_heads[n_]
+                oracle.attention_bwd(qq, kk, vv, fa_inputs.to_f64(dout[b:b + 1, h:h + 1]),
+                                     causal=w.causal, scale=w.scale, window=w.window,
+                                     n_sink=w.n_sink, alibi_slopes=sl)
+            else:
+                oracle.attention_fwd(qq, kk, vv, causal=w.causal, scale=w.scale,
+                                     window=w.window, n_sink=w.n_sink, alibi_slopes=sl)
         return time.perf_counter() - t0
 
     if n_heads <= 0:
@@ -161,7 +177,7 @@ def cpu_baseline(w, q, k, v, n_heads: int, budget_s: float = 20.0):
         n_heads = max(1, min(len(all_heads), int(budget_s / max(t_one, 1e-3))))
     heads = all_heads[:n_heads]
     dt = run([head(b, h) for b, h in heads])
-    flops = algorithmic_flops(w) * len(heads) / (w.B * w.H)
+    flops = work_flops(w) * len(heads) / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(heads)} of {w.B * w.H} heads (all {w.S} rows each) of the same "
                       f"workload, fp64 NumPy, {dt:.2f} s wall"}
@@ -198,13 +214,24 @@ def main():
     slopes = (torch.tensor(alibi_slopes(w.H), dtype=torch.float32, device=dev)
               if w.alibi else None)
 
+    dout = fa_inputs.make_dout(w).to(dev) if w.backward else None
+    if w.backward:
+        o_f, lse_f = fa.flash_attn_fwd(qd, kd, vd, causal=w.causal, window=w.window,
+                                       n_sink=w.n_sink, scale=w.scale, alibi_slopes=slopes)
+        bws = torch.empty(fa.flash_attn_bwd_workspace_bytes(w.B, w.H, w.S), dtype=torch.uint8,
+                          device=dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws = None
     if w.n_split > 1:
         ws = torch.empty(fa.flash_attn_split_workspace_bytes(w.B, w.H, w.S, w.D, w.n_split),
                          dtype=torch.uint8, device=dev)
 
     def step():
-        if w.n_split > 1:
+        if w.backward:
+            fa.flash_attn_bwd(qd, kd, vd, o_f, lse_f, dout, causal=w.causal, window=w.window,
+                              n_sink=w.n_sink, scale=w.scale, alibi_slopes=slopes,
+                              workspace=bws, dq=dq, dk=dk, dv=dv)
+        elif w.n_split > 1:
             fa.flash_attn_fwd_split(qd, kd, vd, n_split=w.n_split, causal=w.causal,
                                     window=w.window, n_sink=w.n_sink, scale=w.scale,
                                     alibi_slopes=slopes, workspace=ws, out=o, lse=lse)
@@ -230,13 +257,15 @@ def main():
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     mean_launch_ms = sum(launch_ms) / len(launch_ms)
 
-    flops = algorithmic_flops(w)
+    flops = work_flops(w)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     e = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
     alg_bytes = (2 * w.H + 2 * w.kv_heads) * w.B * w.S * w.D * e + 4 * w.B * w.H * w.S
+    if w.backward:   # reads q, k, v, o, dO, lse; writes dq, dk, dv
+        alg_bytes = (4 * w.H + 4 * w.kv_heads) * w.B * w.S * w.D * e + 4 * w.B * w.H * w.S
 
     out = {
         "metric": "attention fwd TFLOP/s & % MFMA peak (causal bf16 B4 H16 S4096 D128)",
@@ -252,7 +281,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic: Q, K, V iid N(0,1), numpy default_rng(seed 0), rounded to dtype",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "S": w.S, "D": w.D,
-                   "alibi": w.alibi, "n_split": w.n_split,
+                   "alibi": w.alibi, "n_split": w.n_split, "backward": w.backward,
                    "causal": w.causal, "window": w.window, "n_sink": w.n_sink,
                    "scale": w.scale, "layout": "[B,H,S,D] contiguous",
                    "flops_per_step": flops, "nominal_flops_per_step": nominal_flops(w),

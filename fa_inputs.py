@@ -47,6 +47,7 @@ class Workload:
     H_kv: int = 0             # key/value heads (0: same as H)
     alibi: bool = False       # ALiBi bias with the Lesson 91 deck's slopes
     n_split: int = 1          # key ranges per query block (partials + merge)
+    backward: bool = False    # time the backward pass (gradients from a forward's O, LSE)
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -92,6 +93,10 @@ EXTENSIONS = {
     "split4_causal_b1h8s4096d128_bf16": Workload(
         "split4_causal_b1h8s4096d128_bf16", 1, 8, 4096, 128, "bf16", True,
         1.0 / math.sqrt(128), n_split=4),
+    # The backward pass of the headline shape (dO drawn after Q, K, V).
+    "bwd_causal_b4h16s4096d128_bf16": Workload(
+        "bwd_causal_b4h16s4096d128_bf16", 4, 16, 4096, 128, "bf16", True,
+        1.0 / math.sqrt(128), backward=True),
 }
 ALL_WORKLOADS = {**WORKLOADS, **EXTENSIONS}
 
@@ -118,6 +123,14 @@ def make_qkv(B: int, H: int, S: int, D: int, dtype: str, seed: int = 0,
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.S, w.D, w.dtype, w.seed, w.lab3_draw, w.H_kv)
+
+
+def make_dout(w: Workload):
+    """The upstream gradient dO [B, H, S, D] of a backward workload: N(0, 1) from
+    default_rng(seed + 1), rounded to the dtype like Q, K, V."""
+    rng = np.random.default_rng(w.seed + 1)
+    a = rng.standard_normal(size=(w.B, w.H, w.S, w.D), dtype=np.float32)
+    return torch.from_numpy(a).to(DTYPES[w.dtype]).contiguous()
 
 
 def lab3_example():

@@ -88,7 +88,7 @@ def _sample_rows(S, rng, n=192):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", list(fa_inputs.ALL_WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in fa_inputs.ALL_WORKLOADS.items() if not w.backward])
 def test_workload_parity(name):
     w = fa_inputs.ALL_WORKLOADS[name]
     _say(f"workload {name}: generating inputs")
