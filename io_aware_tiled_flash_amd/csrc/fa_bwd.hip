@@ -29,6 +29,8 @@
 #include "fa_kernel.h"
 #include "fa_lds.h"
 
+#include <type_traits>
+
 namespace fa {
 
 namespace {
@@ -167,8 +169,11 @@ void fa_bwd_dq_kernel(BwdParams p) {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
 
-  __shared__ __attribute__((aligned(1024))) T ks[TILE];
-  __shared__ __attribute__((aligned(1024))) T vs[TILE];
+  // two K/V buffer pairs: block it+1 lands while block it is computed
+  __shared__ __attribute__((aligned(1024))) T k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v1s[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -217,13 +222,24 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_iter = br.count();
-  for (int it = 0; it < n_iter; ++it) {
+  if (n_iter > 0) {
+    dma.load(k0s, Kh, br.kb(0) * BC, S, wave);
+    dma.load(v0s, Vh, br.kb(0) * BC, S, wave);
+  }
+  wait_vmem<0>();
+  __syncthreads();
+  // Block `it` from buffer pair PAR while block it+1 loads into the other;
+  // the loop is unrolled by two so every LDS access names its buffer.
+  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const T* ks = PAR == 0 ? k0s : k1s;
+    const T* vs = PAR == 0 ? v0s : v1s;
+    if (it + 1 < n_iter) {
+      const int k1 = br.kb(it + 1) * BC;
+      dma.load(PAR == 0 ? k1s : k0s, Kh, k1, S, wave);
+      dma.load(PAR == 0 ? v1s : v0s, Vh, k1, S, wave);
+    }
     const int k0 = br.kb(it) * BC;
-    dma.load(ks, Kh, k0, S, wave);
-    dma.load(vs, Vh, k0, S, wave);
-    wait_vmem<0>();
-    __syncthreads();
-
     f32x16 sT[NT], pT[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -264,8 +280,15 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int dt = 0; dt < NDT; ++dt)
           dq[dt] = Tr::mma(lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]), dsb[t][u], dq[dt]);
       }
+    wait_vmem<0>();
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 2 <= n_iter; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
+  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
   if (i < S) store_rowT<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)i * D, dq, h, p.scale);
 }
 
@@ -285,8 +308,11 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
 
-  __shared__ __attribute__((aligned(1024))) T qs[TILE];
-  __shared__ __attribute__((aligned(1024))) T dos[TILE];
+  // two Q/dO buffer pairs: the next query block lands while this one is computed
+  __shared__ __attribute__((aligned(1024))) T q0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T d0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T q1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T d1s[TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -326,84 +352,116 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   int qfirst, qlast;
   query_range(p, k_lo, min(k_lo + BK, S) - 1, BQ, qfirst, qlast);
 
-  for (int gi = 0; gi < p.G; ++gi) {
-    const int bh = bkv * p.G + gi;   // query head (b * H + h)
+  // steps: (query head of the group gi, query block qb) in order, n_q blocks per head
+  const int n_q = qlast - qfirst + 1;
+  const int n_iter = n_q > 0 ? p.G * n_q : 0;
+  auto tile_src = [&](int it, const T*& Qh, const T*& dOh, int& bh, int& q0)
+      __attribute__((always_inline)) {
+    const int gi = it / n_q;
+    bh = bkv * p.G + gi;   // query head (b * H + h)
+    q0 = (qfirst + it - gi * n_q) * BQ;
     const size_t head = (size_t)bh * S * D;
-    const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-    const T* __restrict__ dOh = reinterpret_cast<const T*>(p.dout) + head;
+    Qh = reinterpret_cast<const T*>(p.q) + head;
+    dOh = reinterpret_cast<const T*>(p.dout) + head;
+  };
+  if (n_iter > 0) {
+    const T *Qh, *dOh;
+    int bh0, q00;
+    tile_src(0, Qh, dOh, bh0, q00);
+    dma.load(q0s, Qh, q00, S, wave);
+    dma.load(d0s, dOh, q00, S, wave);
+  }
+  wait_vmem<0>();
+  __syncthreads();
+  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    const T* qs = PAR == 0 ? q0s : q1s;
+    const T* dos = PAR == 0 ? d0s : d1s;
+    const T *Qh_, *dOh_;
+    int bh, q0;
+    tile_src(it, Qh_, dOh_, bh, q0);
     const float* __restrict__ lse = p.lse + (size_t)bh * S;
     const float* __restrict__ dl = p.delta + (size_t)bh * S;
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
-    for (int qb = qfirst; qb <= qlast; ++qb) {
-      const int q0 = qb * BQ;
-      dma.load(qs, Qh, q0, S, wave);
-      dma.load(dos, dOh, q0, S, wave);
-      // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3)
-      f32x4 l2[NT][4], dd[NT][4];
+    // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3)
+    f32x4 l2[NT][4], dd[NT][4];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = q0 + 32 * t + 8 * g + 4 * h;
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = q0 + 32 * t + 8 * g + 4 * h;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool ok = r0 + e < S;
-            l2[t][g][e] = ok ? lse[r0 + e] * kLog2e : __builtin_inff();
-            dd[t][g][e] = ok ? dl[r0 + e] : 0.f;
-          }
-        }
-      wait_vmem<0>();
-      __syncthreads();
-
-      // the whole (block, key block) visible?
-      bool full = (q0 + BQ <= S) && (k_lo + BK <= S);
-      if (p.causal) {
-        full = full && (q0 >= k_lo + BK - 1);
-        if (p.window > 0)
-          full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x16 sc, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[r] = 0.f;
-          dp[r] = 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          sc = Tr::mma(lds_row8(qs + 32 * t * D + ro.off[s]), kf[s], sc);
-          dp = Tr::mma(lds_row8(dos + 32 * t * D + ro.off[s]), vf[s], dp);
-        }
-        // rows i = q0 + 32 t + 8 g + 4 h + e, key j
-        f32x16 pm, ds;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int g = r >> 2, e = r & 3;
-          const int i = q0 + 32 * t + 8 * g + 4 * h + e;
-          float x = p.c * sc[r] - l2[t][g][e];
-          if (ALIBI) x -= b2 * fabsf((float)(i - j));
-          float pr = fast_exp2(x);
-          if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
-          pm[r] = pr;
-          ds[r] = pr * (dp[r] - dd[t][g][e]);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const v8 pb = pack8<T>(pm, u);
-          const v8 db = pack8<T>(ds, u);
-          const T* qq = qs + (32 * t + 16 * u) * D;
-          const T* oo = dos + (32 * t + 16 * u) * D;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            dv[dt] = Tr::mma(lds_tr8(oo + tro.lo[dt], oo + tro.hi[dt]), pb, dv[dt]);
-            dk[dt] = Tr::mma(lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]), db, dk[dt]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = r0 + e < S;
+          l2[t][g][e] = ok ? lse[r0 + e] * kLog2e : __builtin_inff();
+          dd[t][g][e] = ok ? dl[r0 + e] : 0.f;
         }
       }
-      __syncthreads();
+    // The next tile's loads go out after the row loads above: loads complete
+    // in order, so waiting for lse / delta does not wait for the tile.
+    if (it + 1 < n_iter) {
+      const T *Qn, *dOn;
+      int bhn, qn;
+      tile_src(it + 1, Qn, dOn, bhn, qn);
+      dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
+      dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
     }
+
+    // the whole (block, key block) visible?
+    bool full = (q0 + BQ <= S) && (k_lo + BK <= S);
+    if (p.causal) {
+      full = full && (q0 >= k_lo + BK - 1);
+      if (p.window > 0)
+        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      f32x16 sc, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sc = Tr::mma(lds_row8(qs + 32 * t * D + ro.off[s]), kf[s], sc);
+        dp = Tr::mma(lds_row8(dos + 32 * t * D + ro.off[s]), vf[s], dp);
+      }
+      // rows i = q0 + 32 t + 8 g + 4 h + e, key j
+      f32x16 pm, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = r >> 2, e = r & 3;
+        const int i = q0 + 32 * t + 8 * g + 4 * h + e;
+        float x = p.c * sc[r] - l2[t][g][e];
+        if (ALIBI) x -= b2 * fabsf((float)(i - j));
+        float pr = fast_exp2(x);
+        if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
+        pm[r] = pr;
+        ds[r] = pr * (dp[r] - dd[t][g][e]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v8 pb = pack8<T>(pm, u);
+        const v8 db = pack8<T>(ds, u);
+        const T* qq = qs + (32 * t + 16 * u) * D;
+        const T* oo = dos + (32 * t + 16 * u) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = Tr::mma(lds_tr8(oo + tro.lo[dt], oo + tro.hi[dt]), pb, dv[dt]);
+          dk[dt] = Tr::mma(lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]), db, dk[dt]);
+        }
+      }
+    }
+    wait_vmem<0>();
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 2 <= n_iter; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
   }
+  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
   if (j < S) {
     store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
     store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);
