@@ -108,18 +108,35 @@ struct Core {
     tau_raw = kTau / c;
   }
 
-  // S^T = K Q^T for the K tile at ks.
+  // S^T = K Q^T for the K tile at ks. The two 32-key sub-tiles alternate
+  // (independent accumulators back to back), and the K fragment reads run
+  // kQkAhead MFMAs ahead of their use: left to itself the scheduler keeps only
+  // one or two reads in flight, and each MFMA then waits out an LDS latency.
+  static constexpr int kQkAhead = 4;
   __device__ __forceinline__ void qk(f32x16 (&acc)[NT], const T* ks) const {
+    v8 a[NS][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        a[s][t] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(ks + 32 * t * D + koff[s]));
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        v8 a = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(ks + 32 * t * D + koff[s]));
-        acc[t] = Tr::mma(a, qf[s], acc[t]);
-      }
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = Tr::mma(a[s][t], qf[s], acc[t]);
+    // Schedule: kQkAhead reads, then (one MFMA, one read) pairs, then the
+    // last MFMAs. Mask bits: 0x100 LDS read, 0x008 MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
+#pragma unroll
+    for (int u = 0; u < NS * NT - kQkAhead; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
   }
 
   // Mask the scores of a partially visible block: key j = k0 + 4h + e,
@@ -152,12 +169,21 @@ struct Core {
   // Online softmax with lazy rescale: turns the (masked) scores into p,
   // adds them to l and packs them into the B operands of the PV MFMA.
   __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2]) {
-    float mt = acc[0][0];
+    // Row max in four independent chains of three-input maxes, then joined:
+    // one chain of dependent maxes would sit on the path from the last QK
+    // MFMA to the first exponential.
+    float m4[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int k = 0; k < 4; ++k) {
+      float a = acc[0][k];
 #pragma unroll
-      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mt = fmaxf(mt, acc[t][r]);
-    mt = xhalf_max(mt);
+      for (int e = k + 4; e < 16 * NT; e += 8) {
+        const float x = acc[e >> 4][e & 15];
+        a = (e + 4 < 16 * NT) ? fmaxf(fmaxf(a, x), acc[(e + 4) >> 4][(e + 4) & 15]) : fmaxf(a, x);
+      }
+      m4[k] = a;
+    }
+    const float mt = xhalf_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     const float m_new = fmaxf(m_run, mt);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + tau_raw)) {
       const float mc_new = (m_new == kNegInf) ? 0.f : m_new * c;
@@ -278,7 +304,8 @@ void fa_fwd_fast_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: LDS destinations of the tile loads (m0) stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // With a key split, work-group id = split * (nqb * BH) + (the id of the
   // unsplit launch); each split takes a contiguous share of the key blocks.

@@ -65,14 +65,16 @@ struct TileDma {
 
   __device__ __forceinline__ void load(T* lds_tile, const T* __restrict__ g, int k0, int S,
                                        int wave) const {
-    // Base and size are wave-uniform; readfirstlane keeps them in scalar
-    // registers, where the descriptor must live.
-    const uint64_t base = reinterpret_cast<uint64_t>(g + (size_t)k0 * D);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-    const int bytes = __builtin_amdgcn_readfirstlane((S - k0) * D * (int)sizeof(T));
+    // Base and size are wave-uniform and the descriptor must sit in scalar
+    // registers: the head pointer goes through readfirstlane before the
+    // block offset is added, so the per-block address arithmetic is scalar.
+    const uint64_t g64 = reinterpret_cast<uint64_t>(g);
+    const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g64);
+    const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g64 >> 32));
+    const uint64_t base = (((uint64_t)ghi << 32) | glo) + (uint64_t)(uint32_t)k0 * (D * sizeof(T));
+    const int bytes = (S - k0) * D * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, bytes, kBufferFlags);
+        reinterpret_cast<void*>(base), (short)0, bytes, kBufferFlags);
 #pragma unroll
     for (int n = 0; n < NI; ++n)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + (wave * NI + n) * 512),
