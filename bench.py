@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # the counters were taken on. Any other source tree reports traffic = null.
 KERNEL_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_fwd_fast.hip",
                   "io_aware_tiled_flash_amd/csrc/fa_device.h",
-                  "io_aware_tiled_flash_amd/csrc/fa_kernel.h"]
+                  "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
+                  "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
     ("causal_b4h16s4096d128_bf16",
      "7b5ecdae0417b67f2e04ba55d435343d5390bcb3e6d11bb43324f2bd1befd312"):
@@ -59,8 +60,11 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # The board takes on the order of a hundred back-to-back launches of the
+    # headline shape (~30 ms of load) to leave its idle power state: the
+    # first 20 launches run ~20 % slower than the steady state.
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=0,

@@ -111,7 +111,21 @@ __device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, 
 // block of a head runs on one XCD; the heads are spread so that each XCD
 // holds a contiguous run of them, which keeps query heads that share a
 // key/value head (consecutive heads) on one XCD's L2 as well.
+//
+// Without the causal triangle (no mask, or a sliding window) every query
+// block costs about the same, and the order is chosen for the L2 instead:
+// each XCD takes a contiguous run of heads and walks each head's query
+// blocks in order, so the work-groups resident on an XCD at one time cover
+// one or two heads, whose keys and values fit its L2 (rank-major order would
+// spread them over every head of the XCD, and a window's keys would be
+// fetched again for each of them).
 __device__ __forceinline__ void wg_coords(const FwdParams& p, int id, int& qb, int& bh) {
+  if ((!p.causal || p.window > 0) && (p.BH & 7) == 0) {
+    const int l = id >> 3;
+    bh = (id & 7) * (p.BH >> 3) + l / p.nqb;
+    qb = l % p.nqb;
+    return;
+  }
   const int x = id % p.BH;
   const int rank = id / p.BH;
   bh = (p.BH & 7) ? x : (x & 7) * (p.BH >> 3) + (x >> 3);
