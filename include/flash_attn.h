@@ -189,8 +189,10 @@ int flash_attn_merge(const float* o_parts, const float* lse_parts, int64_t n_par
  *                  dtype: as in flash_attn_fwd_ext, with dtype FA_BF16 /
  *                  FA_F16 and D 64 or 128 (else FA_ERR_UNSUPPORTED).
  * workspace      : device scratch of >= flash_attn_bwd_workspace_bytes(B, H, S)
- *                  bytes (per-row rowsum(dout * o)), 16-byte aligned; contents
- *                  on entry do not matter. Calls sharing it must not overlap.
+ *                  bytes (two per-row fp32 arrays: rowsum(dout * o) and
+ *                  lse * log2(e), S padded to a multiple of 128 rows per head),
+ *                  16-byte aligned; contents on entry do not matter. Calls
+ *                  sharing it must not overlap.
  * Precision: fp32 accumulation; P and dS rounded to `dtype` before their
  * products (like P in the forward); outputs rounded once.
  * Outputs must not overlap any input, each other or the workspace. Two

@@ -304,7 +304,8 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   const int64_t rows = B * H * S;
   const uint64_t tb = (uint64_t)(rows * D * e), kvb = tb / (uint64_t)(H / H_kv);
   const uint64_t lb = (uint64_t)rows * 4;
-  const int64_t need = (rows * 4 + 255) / 256 * 256;
+  const int64_t need = flash_attn_bwd_workspace_bytes(B, H, S);
+  if (need < 0) return FA_ERR_INVALID;
   if (workspace_bytes < need) return fail(FA_ERR_INVALID, "workspace too small");
   struct Region { const void* p; uint64_t n; };
   const Region outs[] = {{dq, tb}, {dk, kvb}, {dv, kvb}, {workspace, (uint64_t)need}};
@@ -336,7 +337,10 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  const int64_t sp = nb * br;   // rows per head of the two workspace arrays
   p.delta = static_cast<float*>(workspace);
+  p.lse2 = static_cast<float*>(workspace) + B * H * sp;
+  p.Sp = (int)sp;
   p.alibi = alibi_slopes;
   p.S = (int)S;
   p.BH = (int)(B * H);
@@ -363,11 +367,15 @@ int64_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
     fail(FA_ERR_INVALID, "B, H and S must be >= 1");
     return -1;
   }
-  if (B > INT64_MAX / 8 / H || B * H > INT64_MAX / 8 / S) {
+  // two fp32 arrays [B*H][Sp] (per-row delta and lse * log2(e)), Sp = S
+  // rounded up to the dq kernel's block of rows
+  const int64_t br = fa::bwd_tile_rows();
+  if (S > INT64_MAX / 16 || B > INT64_MAX / 16 / H || B * H > INT64_MAX / 16 / (S + br)) {
     fail(FA_ERR_INVALID, "B*H*S overflows");
     return -1;
   }
-  return (B * H * S * 4 + 255) / 256 * 256;
+  const int64_t sp = (S + br - 1) / br * br;
+  return (2 * B * H * sp * 4 + 255) / 256 * 256;
 }
 
 int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -145,17 +145,15 @@ __device__ __forceinline__ void query_range(const BwdParams& p, int k_lo, int k_
   }
 }
 
-__device__ __forceinline__ bool visible_ij(const BwdParams& p, int i, int j) {
-  const bool in_range = (i < p.S) & (j < p.S);
-  const bool in_window = (p.window == 0) | ((i - j) < p.window) | (j < p.n_sink);
-  return in_range & ((p.causal == 0) | ((j <= i) & in_window));
-}
-
 }  // namespace
 
 // ------------------------------------------------------------------------ //
 // dq kernel
 // ------------------------------------------------------------------------ //
+// Besides dQ, it writes the two per-row arrays the dkv kernel reads, padded to
+// Sp rows per head so that the dkv kernel's 16-byte loads need no bounds
+// checks: delta (0 past the sequence end) and lse * log2(e) (+inf there, so
+// that rows past the end get P = 0 without a mask).
 template <typename T, int D, bool ALIBI>
 __global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dq_kernel(BwdParams p) {
@@ -175,14 +173,15 @@ void fa_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) T k1s[TILE];
   __shared__ __attribute__((aligned(1024))) T v1s[TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int bh = (int)blockIdx.x % p.BH;
   const int rank = (int)blockIdx.x / p.BH;
   const int qb = p.causal ? (p.nqb - 1 - rank) : rank;
   const int S = p.S;
   const int q_lo = qb * BR;
-  const int i = q_lo + 32 * wave + col;
+  const int i = q_lo + 32 * wave + col;   // < nqb * BR = Sp
   const size_t head = (size_t)bh * S * D;
   const size_t kv_head = (size_t)(bh / p.G) * S * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
@@ -202,9 +201,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)df[s][e], (float)of[e], dpart);
   }
-  const float delta = xhalf_sum(dpart);
-  const float lse2 = (i < S) ? p.lse[(size_t)bh * S + i] * kLog2e : 0.f;
-  if (h == 0 && i < S) p.delta[(size_t)bh * S + i] = delta;
+  const bool row_ok = i < S;
+  const float delta = row_ok ? xhalf_sum(dpart) : 0.f;
+  const float lse2 = row_ok ? p.lse[(size_t)bh * S + i] * kLog2e : __builtin_inff();
+  if (h == 0) {
+    p.delta[(size_t)bh * p.Sp + i] = delta;
+    p.lse2[(size_t)bh * p.Sp + i] = lse2;
+  }
   const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
 
   RowOffsets<D> ro;
@@ -220,6 +223,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
 
+  // Per-lane mask bounds in units of e = 32 t + 8 g + r4 (key j = k0 + 4 h + e),
+  // as in the forward kernel: keep iff e <= hi and (e >= lo or e <= sk).
+  const int big = 1 << 30;
+  const int hi0 = p.causal ? min(i, S - 1) : S - 1;
+  const int lo0 = p.window > 0 ? i - p.window + 1 : -big;
+  const int sk0 = p.window > 0 ? p.n_sink - 1 : -big;
+
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_iter = br.count();
   if (n_iter > 0) {
@@ -229,9 +239,11 @@ void fa_bwd_dq_kernel(BwdParams p) {
   wait_vmem<0>();
   __syncthreads();
   // Block `it` from buffer pair PAR while block it+1 loads into the other;
-  // the loop is unrolled by two so every LDS access names its buffer.
-  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+  // MASK selects the masked variant at compile time (partially visible
+  // blocks sit at the two ends of the visiting order, as in the forward).
+  auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
+    constexpr bool MASK = decltype(mask)::value;
     const T* ks = PAR == 0 ? k0s : k1s;
     const T* vs = PAR == 0 ? v0s : v1s;
     if (it + 1 < n_iter) {
@@ -254,17 +266,21 @@ void fa_bwd_dq_kernel(BwdParams p) {
         pT[t] = Tr::mma(lds_row8(vs + 32 * t * D + ro.off[s]), df[s], pT[t]);
       }
     }
-    const bool full = block_full<BR, BC>(q_lo, k0, S, p.causal, p.window, p.n_sink);
+    const int jb = k0 + 4 * h;
+    const int hi = hi0 - jb, lo = lo0 - jb, sk = sk0 - jb;
     v8 dsb[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = k0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-        float x = p.c * sT[t][r] - lse2;
-        if (ALIBI) x -= b2 * fabsf((float)(i - j));
+        const int e = 32 * t + 8 * (r >> 2) + (r & 3);
+        float x;
+        if (ALIBI)
+          x = __builtin_fmaf(sT[t][r], p.c, -b2 * fabsf((float)(i - jb - e))) - lse2;
+        else
+          x = __builtin_fmaf(sT[t][r], p.c, -lse2);
         float pr = fast_exp2(x);
-        if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
+        if (MASK) pr = ((e <= hi) & ((e >= lo) | (e <= sk))) ? pr : 0.f;
         sT[t][r] = pr * (pT[t][r] - delta);   // dS^T
       }
       dsb[t][0] = pack8<T>(sT[t], 0);
@@ -283,13 +299,25 @@ void fa_bwd_dq_kernel(BwdParams p) {
     wait_vmem<0>();
     __syncthreads();
   };
-  int it = 0;
-  for (; it + 2 <= n_iter; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-  }
-  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
-  if (i < S) store_rowT<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)i * D, dq, h, p.scale);
+  auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
+    int it = b;
+    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+    for (; it + 2 <= e; it += 2) {
+      step(std::integral_constant<int, 0>{}, mask, it);
+      step(std::integral_constant<int, 1>{}, mask, it + 1);
+    }
+    if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+  };
+  int f0 = 0;
+  while (f0 < n_iter && !block_full<BR, BC>(q_lo, br.kb(f0) * BC, S, p.causal, p.window, p.n_sink))
+    ++f0;
+  int f1 = f0;
+  while (f1 < n_iter && block_full<BR, BC>(q_lo, br.kb(f1) * BC, S, p.causal, p.window, p.n_sink))
+    ++f1;
+  segment(std::true_type{}, 0, f0);
+  segment(std::false_type{}, f0, f1);
+  segment(std::true_type{}, f1, n_iter);
+  if (row_ok) store_rowT<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)i * D, dq, h, p.scale);
 }
 
 // ------------------------------------------------------------------------ //
@@ -314,7 +342,8 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) T q1s[TILE];
   __shared__ __attribute__((aligned(1024))) T d1s[TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int BHkv = p.BH / p.G;
   const int bkv = (int)blockIdx.x % BHkv;
@@ -351,6 +380,14 @@ void fa_bwd_dkv_kernel(BwdParams p) {
 
   int qfirst, qlast;
   query_range(p, k_lo, min(k_lo + BK, S) - 1, BQ, qfirst, qlast);
+  // Mask of a partially visible (query block, key block) pair, for row
+  // i = q0 + 4 h + e (e = 32 t + 8 g + r4) and this lane's key j: keep iff
+  // i >= j and (i - j < window or j < n_sink). Rows past the sequence end
+  // need no mask (their lse * log2(e) is +inf), nor do keys past it (their
+  // K / V rows are zero and their dK, dV are never stored).
+  const int big = 1 << 30;
+  const bool sinkj = p.window > 0 && j < p.n_sink;
+  const int wlen = p.window > 0 ? p.window : big;
 
   // steps: (query head of the group gi, query block qb) in order, n_q blocks per head
   const int n_q = qlast - qfirst + 1;
@@ -364,6 +401,15 @@ void fa_bwd_dkv_kernel(BwdParams p) {
     Qh = reinterpret_cast<const T*>(p.q) + head;
     dOh = reinterpret_cast<const T*>(p.dout) + head;
   };
+  auto block_full_kv = [&](int q0) __attribute__((always_inline)) {
+    bool full = true;
+    if (p.causal) {
+      full = q0 >= k_lo + BK - 1;
+      if (p.window > 0)
+        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
+    }
+    return full;
+  };
   if (n_iter > 0) {
     const T *Qh, *dOh;
     int bh0, q00;
@@ -373,49 +419,37 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   }
   wait_vmem<0>();
   __syncthreads();
-  auto step = [&](auto par, int it) __attribute__((always_inline)) {
+  auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
+    constexpr bool MASK = decltype(mask)::value;
     const T* qs = PAR == 0 ? q0s : q1s;
     const T* dos = PAR == 0 ? d0s : d1s;
     const T *Qh_, *dOh_;
     int bh, q0;
     tile_src(it, Qh_, dOh_, bh, q0);
-    const float* __restrict__ lse = p.lse + (size_t)bh * S;
-    const float* __restrict__ dl = p.delta + (size_t)bh * S;
+    // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3), from the
+    // padded per-row arrays (16-byte aligned, no bounds checks needed)
+    const size_t rbase = (size_t)bh * p.Sp + q0 + 4 * h;
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
-    // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3)
-    f32x4 l2[NT][4], dd[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = q0 + 32 * t + 8 * g + 4 * h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = r0 + e < S;
-          l2[t][g][e] = ok ? lse[r0 + e] * kLog2e : __builtin_inff();
-          dd[t][g][e] = ok ? dl[r0 + e] : 0.f;
-        }
-      }
-    // The next tile's loads go out after the row loads above: loads complete
-    // in order, so waiting for lse / delta does not wait for the tile.
-    if (it + 1 < n_iter) {
-      const T *Qn, *dOn;
-      int bhn, qn;
-      tile_src(it + 1, Qn, dOn, bhn, qn);
-      dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
-      dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
-    }
-
-    // the whole (block, key block) visible?
-    bool full = (q0 + BQ <= S) && (k_lo + BK <= S);
-    if (p.causal) {
-      full = full && (q0 >= k_lo + BK - 1);
-      if (p.window > 0)
-        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
-    }
+    const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
+    const int ewin = emin + wlen;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      f32x4 l2[4], dd[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l2[g] = *reinterpret_cast<const f32x4*>(p.lse2 + rbase + 32 * t + 8 * g);
+        dd[g] = *reinterpret_cast<const f32x4*>(p.delta + rbase + 32 * t + 8 * g);
+      }
+      // The next tile's loads go out after the first row loads: loads
+      // complete in order, so waiting for lse / delta does not wait for it.
+      if (t == 0 && it + 1 < n_iter) {
+        const T *Qn, *dOn;
+        int bhn, qn;
+        tile_src(it + 1, Qn, dOn, bhn, qn);
+        dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
+        dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
+      }
       f32x16 sc, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -427,18 +461,20 @@ void fa_bwd_dkv_kernel(BwdParams p) {
         sc = Tr::mma(lds_row8(qs + 32 * t * D + ro.off[s]), kf[s], sc);
         dp = Tr::mma(lds_row8(dos + 32 * t * D + ro.off[s]), vf[s], dp);
       }
-      // rows i = q0 + 32 t + 8 g + 4 h + e, key j
       f32x16 pm, ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int g = r >> 2, e = r & 3;
-        const int i = q0 + 32 * t + 8 * g + 4 * h + e;
-        float x = p.c * sc[r] - l2[t][g][e];
-        if (ALIBI) x -= b2 * fabsf((float)(i - j));
+        const int g = r >> 2, e4 = r & 3;
+        const int e = 32 * t + 8 * g + e4;
+        float x;
+        if (ALIBI)
+          x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
+        else
+          x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
         float pr = fast_exp2(x);
-        if (!full) pr = visible_ij(p, i, j) ? pr : 0.f;
+        if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
         pm[r] = pr;
-        ds[r] = pr * (dp[r] - dd[t][g][e]);
+        ds[r] = pr * (dp[r] - dd[g][e4]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -452,16 +488,40 @@ void fa_bwd_dkv_kernel(BwdParams p) {
           dk[dt] = Tr::mma(lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]), db, dk[dt]);
         }
       }
+      // keep the two 32-row halves apart: hoisting the second half's LDS
+      // reads into the first runs the register file out
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmem<0>();
     __syncthreads();
   };
-  int it = 0;
-  for (; it + 2 <= n_iter; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
+  // Steps [b, e) of one segment; the buffer pair alternates with it & 1.
+  auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
+    int it = b;
+    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+    for (; it + 2 <= e; it += 2) {
+      step(std::integral_constant<int, 0>{}, mask, it);
+      step(std::integral_constant<int, 1>{}, mask, it + 1);
+    }
+    if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+  };
+  // Per query head, the query blocks run [partially visible][fully
+  // visible][partially visible] (the causal diagonal first, the window's end
+  // last), so each head is three segments and the common step carries no mask
+  // code and no branch: a branch per step would make the compiler copy the
+  // dK / dV accumulators at every join.
+  if (n_q > 0) {
+    int f0 = 0;
+    while (f0 < n_q && !block_full_kv((qfirst + f0) * BQ)) ++f0;
+    int f1 = f0;
+    while (f1 < n_q && block_full_kv((qfirst + f1) * BQ)) ++f1;
+    for (int gi = 0; gi < p.G; ++gi) {
+      const int b = gi * n_q;
+      segment(std::true_type{}, b, b + f0);
+      segment(std::false_type{}, b + f0, b + f1);
+      segment(std::true_type{}, b + f1, b + n_q);
+    }
   }
-  if (it < n_iter) step(std::integral_constant<int, 0>{}, it);
   if (j < S) {
     store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
     store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);

@@ -47,9 +47,11 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;        // workspace: rowsum(dO * O) [BH][S]
+  float* delta;        // workspace: rowsum(dO * O) [BH][Sp], 0 past S
+  float* lse2;         // workspace: lse * log2(e) [BH][Sp], +inf past S
   const float* alibi;  // per-query-head slopes [H], or null
   int S, BH, H, G;     // G = query heads per key/value head
+  int Sp;              // rows per head of the workspace arrays (S rounded up to the dq block)
   int nqb, nkb;        // query blocks of the dq kernel, key blocks of the dkv kernel
   int causal, window, n_sink;
   float c, scale;

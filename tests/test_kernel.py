@@ -509,7 +509,7 @@ def _bwd_case(B, H, Hkv, S, D, dtype, causal, window, n_sink, scale, seed, slope
 @pytest.mark.parametrize("D", [64, 128])
 def test_backward(dtype, D):
     for S in (1, 63, 200, 333):
-        for causal, window, n_sink in MASKS[:4]:
+        for causal, window, n_sink in MASKS:
             _bwd_case(1, 2, 2, S, D, dtype, causal, window, n_sink, 1.0 / math.sqrt(D),
                       seed=S + D, label=f"{dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
 
@@ -524,6 +524,9 @@ def test_backward_grouped_heads_alibi_scale(dtype):
               slopes=ORACLE.alibi_slopes(4), label="alibi")
     _bwd_case(1, 2, 2, 150, 64, dtype, True, 0, 0, -0.2, seed=6, label="negative scale")
     _bwd_case(1, 2, 2, 150, 64, dtype, False, 0, 0, 0.0, seed=7, label="zero scale")
+    # a window wide enough that a key block sees masked, then fully visible,
+    # then masked query blocks, repeated over the query heads of each group
+    _bwd_case(1, 4, 2, 700, 128, dtype, True, 300, 4, 0.088, seed=8, label="gqa window")
 
 
 def test_backward_headline_shape_sampled():
