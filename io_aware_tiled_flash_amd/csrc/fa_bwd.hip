@@ -145,6 +145,23 @@ __device__ __forceinline__ void query_range(const BwdParams& p, int k_lo, int k_
   }
 }
 
+// Scheduling groups for a run of N MFMAs fed by LDS reads (PER reads per
+// MFMA): AHEAD MFMAs' worth of reads first, then one MFMA and its successor's
+// reads in turn, then the last MFMAs. With one wave per SIMD nothing else
+// hides the LDS latency, and left to itself the scheduler issues each read
+// right before the MFMA that consumes it. Mask bits: 0x100 LDS read, 0x008
+// MFMA.
+template <int N, int PER, int AHEAD>
+__device__ __forceinline__ void lds_mfma_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, PER * AHEAD, 0);
+#pragma unroll
+  for (int u = 0; u < N - AHEAD; ++u) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ //
@@ -260,12 +277,19 @@ void fa_bwd_dq_kernel(BwdParams p) {
         sT[t][r] = 0.f;
         pT[t][r] = 0.f;
       }
+      v8 ka[NS], va[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sT[t] = Tr::mma(lds_row8(ks + 32 * t * D + ro.off[s]), qf[s], sT[t]);
-        pT[t] = Tr::mma(lds_row8(vs + 32 * t * D + ro.off[s]), df[s], pT[t]);
+        ka[s] = lds_row8(ks + 32 * t * D + ro.off[s]);
+        va[s] = lds_row8(vs + 32 * t * D + ro.off[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sT[t] = Tr::mma(ka[s], qf[s], sT[t]);
+        pT[t] = Tr::mma(va[s], df[s], pT[t]);
       }
     }
+    lds_mfma_pipeline<2 * NT * NS, 1, 6>();
     const int jb = k0 + 4 * h;
     const int hi = hi0 - jb, lo = lo0 - jb, sk = sk0 - jb;
     v8 dsb[NT][2];
@@ -287,15 +311,22 @@ void fa_bwd_dq_kernel(BwdParams p) {
       dsb[t][1] = pack8<T>(sT[t], 1);
     }
     // dQ^T += K^T dS^T
+    v8 kT[NT][2][NDT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const T* kk = ks + (32 * t + 16 * u) * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          dq[dt] = Tr::mma(lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]), dsb[t][u], dq[dt]);
+        for (int dt = 0; dt < NDT; ++dt) kT[t][u][dt] = lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]);
       }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) dq[dt] = Tr::mma(kT[t][u][dt], dsb[t][u], dq[dt]);
+    lds_mfma_pipeline<2 * NT * NDT, 2, 4>();
     wait_vmem<0>();
     __syncthreads();
   };
@@ -456,11 +487,20 @@ void fa_bwd_dkv_kernel(BwdParams p) {
         sc[r] = 0.f;
         dp[r] = 0.f;
       }
+      // operands read into arrays first: with the reads inline the register
+      // allocator gave every read the same registers, serialising them
+      v8 qa[NS], da[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sc = Tr::mma(lds_row8(qs + 32 * t * D + ro.off[s]), kf[s], sc);
-        dp = Tr::mma(lds_row8(dos + 32 * t * D + ro.off[s]), vf[s], dp);
+        qa[s] = lds_row8(qs + 32 * t * D + ro.off[s]);
+        da[s] = lds_row8(dos + 32 * t * D + ro.off[s]);
       }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sc = Tr::mma(qa[s], kf[s], sc);
+        dp = Tr::mma(da[s], vf[s], dp);
+      }
+      lds_mfma_pipeline<2 * NS, 1, 6>();
       f32x16 pm, ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -476,18 +516,28 @@ void fa_bwd_dkv_kernel(BwdParams p) {
         pm[r] = pr;
         ds[r] = pr * (dp[r] - dd[g][e4]);
       }
+      v8 oT[2][NDT], qT[2][NDT];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const v8 pb = pack8<T>(pm, u);
-        const v8 db = pack8<T>(ds, u);
         const T* qq = qs + (32 * t + 16 * u) * D;
         const T* oo = dos + (32 * t + 16 * u) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = Tr::mma(lds_tr8(oo + tro.lo[dt], oo + tro.hi[dt]), pb, dv[dt]);
-          dk[dt] = Tr::mma(lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]), db, dk[dt]);
+          oT[u][dt] = lds_tr8(oo + tro.lo[dt], oo + tro.hi[dt]);
+          qT[u][dt] = lds_tr8(qq + tro.lo[dt], qq + tro.hi[dt]);
         }
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v8 pb = pack8<T>(pm, u);
+        const v8 db = pack8<T>(ds, u);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = Tr::mma(oT[u][dt], pb, dv[dt]);
+          dk[dt] = Tr::mma(qT[u][dt], db, dk[dt]);
+        }
+      }
+      lds_mfma_pipeline<4 * NDT, 2, 4>();
       // keep the two 32-row halves apart: hoisting the second half's LDS
       // reads into the first runs the register file out
       __builtin_amdgcn_sched_barrier(0);
