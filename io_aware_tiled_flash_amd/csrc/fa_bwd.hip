@@ -162,6 +162,17 @@ __device__ __forceinline__ void lds_mfma_pipeline() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
+// Direct-to-LDS copy of 64 consecutive fp32 values (one per lane, 4 bytes
+// each) from g to the LDS array lds: issued by one wave.
+__device__ __forceinline__ void rows_to_lds(float* lds, const float* g, int lane) {
+  const uint64_t g64 = reinterpret_cast<uint64_t>(g);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)g64);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(g64 >> 32));
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, 64 * 4, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, (uint32_t)lane * 4u, 0, 0, 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ //
@@ -372,6 +383,9 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) T d0s[TILE];
   __shared__ __attribute__((aligned(1024))) T q1s[TILE];
   __shared__ __attribute__((aligned(1024))) T d1s[TILE];
+  // the block's lse * log2(e) and delta rows, staged with the tiles
+  __shared__ __attribute__((aligned(16))) float r0s[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float r1s[2 * BQ];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -441,12 +455,22 @@ void fa_bwd_dkv_kernel(BwdParams p) {
     }
     return full;
   };
+  // rows [q0, q0 + BQ) of the padded per-row arrays (no bounds checks: q0 +
+  // BQ <= Sp) into dst = [lse * log2(e) | delta]
+  auto rows_dma = [&](float* dst, int bh, int q0) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const size_t rb = (size_t)bh * p.Sp + q0;
+      rows_to_lds(dst, p.lse2 + rb, lane);
+      rows_to_lds(dst + BQ, p.delta + rb, lane);
+    }
+  };
   if (n_iter > 0) {
     const T *Qh, *dOh;
     int bh0, q00;
     tile_src(0, Qh, dOh, bh0, q00);
     dma.load(q0s, Qh, q00, S, wave);
     dma.load(d0s, dOh, q00, S, wave);
+    rows_dma(r0s, bh0, q00);
   }
   wait_vmem<0>();
   __syncthreads();
@@ -455,32 +479,23 @@ void fa_bwd_dkv_kernel(BwdParams p) {
     constexpr bool MASK = decltype(mask)::value;
     const T* qs = PAR == 0 ? q0s : q1s;
     const T* dos = PAR == 0 ? d0s : d1s;
+    const float* rs = PAR == 0 ? r0s : r1s;
     const T *Qh_, *dOh_;
     int bh, q0;
     tile_src(it, Qh_, dOh_, bh, q0);
-    // this lane's rows of the block: q0 + 32 t + 8 g + 4 h + (0..3), from the
-    // padded per-row arrays (16-byte aligned, no bounds checks needed)
-    const size_t rbase = (size_t)bh * p.Sp + q0 + 4 * h;
+    if (it + 1 < n_iter) {
+      const T *Qn, *dOn;
+      int bhn, qn;
+      tile_src(it + 1, Qn, dOn, bhn, qn);
+      dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
+      dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
+      rows_dma(PAR == 0 ? r1s : r0s, bhn, qn);
+    }
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
     const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
     const int ewin = emin + wlen;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4 l2[4], dd[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l2[g] = *reinterpret_cast<const f32x4*>(p.lse2 + rbase + 32 * t + 8 * g);
-        dd[g] = *reinterpret_cast<const f32x4*>(p.delta + rbase + 32 * t + 8 * g);
-      }
-      // The next tile's loads go out after the first row loads: loads
-      // complete in order, so waiting for lse / delta does not wait for it.
-      if (t == 0 && it + 1 < n_iter) {
-        const T *Qn, *dOn;
-        int bhn, qn;
-        tile_src(it + 1, Qn, dOn, bhn, qn);
-        dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
-        dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
-      }
       f32x16 sc, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -501,6 +516,15 @@ void fa_bwd_dkv_kernel(BwdParams p) {
         dp = Tr::mma(da[s], vf[s], dp);
       }
       lds_mfma_pipeline<2 * NS, 1, 6>();
+      // this lane's rows of the block: 32 t + 8 g + 4 h + (0..3); read after
+      // the operand reads above (one more scheduling group of 8 LDS reads)
+      f32x4 l2[4], dd[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l2[g] = *reinterpret_cast<const f32x4*>(rs + 32 * t + 8 * g + 4 * h);
+        dd[g] = *reinterpret_cast<const f32x4*>(rs + BQ + 32 * t + 8 * g + 4 * h);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       f32x16 pm, ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
