@@ -33,25 +33,32 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the forward kernel, measured with rocprofv3 counter runs
-# (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors a 256 MiB device copy
-# of known size gives), keyed by workload and the SHA-256 of the kernel sources
-# the counters were taken on. Any other source tree reports traffic = null.
-KERNEL_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_fwd_fast.hip",
-                  "io_aware_tiled_flash_amd/csrc/fa_device.h",
-                  "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
-                  "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
+# HBM bytes per step measured with rocprofv3 counter runs (FETCH_SIZE scaled
+# x2.0 and WRITE_SIZE x1.0, the factors a 256 MiB device copy of known size
+# gives), keyed by workload and the SHA-256 of the kernel sources the counters
+# were taken on. Any other source tree reports traffic = null.
+FWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_fwd_fast.hip",
+               "io_aware_tiled_flash_amd/csrc/fa_device.h",
+               "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
+               "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
+BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
+               "io_aware_tiled_flash_amd/csrc/fa_device.h",
+               "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
+               "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
+    # forward kernel, 4 waves: FETCH 384461.5 KiB, WRITE 66848.1 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "7b5ecdae0417b67f2e04ba55d435343d5390bcb3e6d11bb43324f2bd1befd312"):
-        2.0 * 222431.9 * 1024 + 1.0 * 66560.8 * 1024,
+     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 855829592,
+    # dq + dkv kernels: FETCH 394002.0 + 364181.9 KiB, WRITE 67584 + 131072 KiB per step
+    ("bwd_causal_b4h16s4096d128_bf16",
+     "4c1e3d67e4c284c291c01f2157309aa63ce57058212b2ab78c9913bf4f1d0fe5"): 1756184448,
 }
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(backward: bool = False) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (BWD_SOURCES if backward else FWD_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -295,7 +302,7 @@ def main():
                    "alg_hbm_GBps": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": MEASURED_TRAFFIC.get((name, kernel_source_hash())),  # bytes per launch
+                     "traffic": MEASURED_TRAFFIC.get((name, kernel_source_hash(w.backward))),  # bytes per step
                      "kernel": kernel_name(fa, w),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
