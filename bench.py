@@ -46,12 +46,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
-    # forward kernel, 4 waves: FETCH 384461.5 KiB, WRITE 66848.1 KiB per launch
+    # forward kernel, 4 waves: FETCH 388976.5 KiB, WRITE 66801.2 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 855829592,
-    # dq + dkv kernels: FETCH 394002.0 + 364181.9 KiB, WRITE 67584 + 131072 KiB per step
+     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 865027277,
+    # dq + dkv kernels: FETCH 394002.3 + 364194.8 KiB, WRITE 67585.2 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "4c1e3d67e4c284c291c01f2157309aa63ce57058212b2ab78c9913bf4f1d0fe5"): 1756184448,
+     "4c1e3d67e4c284c291c01f2157309aa63ce57058212b2ab78c9913bf4f1d0fe5"): 1756212429,
+    # forward kernel, f16 D=64: FETCH 3193.2 KiB, WRITE 2112 KiB per launch
+    ("noncausal_b2h8s1024d64_f16",
+     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 8702300,
 }
 
 
