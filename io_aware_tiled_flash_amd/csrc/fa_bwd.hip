@@ -8,7 +8,8 @@
 //     dV = P^T dO,   dS = P * (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Two kernels, both on v_mfma_f32_32x32x16 for every product:
-//  * dq kernel: one work-group per (query block of 32 * NW rows, query head).
+//  * dq kernel: one work-group per (query block of 32 * NW rows, query head),
+//    two work-groups per CU.
 //    Each wave holds 32 rows of Q and dO in registers, computes its rows'
 //    delta (written to the workspace for the second kernel) and streams the
 //    visible key blocks: S^T = K Q^T and dP^T = V dO^T (K, V rows read from
@@ -183,7 +184,7 @@ __device__ __forceinline__ void rows_to_lds(float* lds, const float* g, int lane
 // checks: delta (0 past the sequence end) and lse * log2(e) (+inf there, so
 // that rows past the end get P = 0 without a mask).
 template <typename T, int D, bool ALIBI>
-__global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int NW = kBwdWaves;
   constexpr int BR = 32 * NW;
@@ -280,13 +281,20 @@ void fa_bwd_dq_kernel(BwdParams p) {
       dma.load(PAR == 0 ? v1s : v0s, Vh, k1, S, wave);
     }
     const int k0 = br.kb(it) * BC;
-    f32x16 sT[NT], pT[NT];
+    const int jb = k0 + 4 * h;
+    const int hi = hi0 - jb, lo = lo0 - jb, sk = sk0 - jb;
+    // One 32-key half at a time (scores, dS, then its share of dQ), with
+    // short read lookaheads: that keeps the kernel within 256 registers, so
+    // two work-groups share a CU and one wave's vector work overlaps the
+    // other's MFMAs (8 % faster than one wave per SIMD with both halves'
+    // scores held at once).
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      f32x16 sT, pT;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sT[t][r] = 0.f;
-        pT[t][r] = 0.f;
+        sT[r] = 0.f;
+        pT[r] = 0.f;
       }
       v8 ka[NS], va[NS];
 #pragma unroll
@@ -296,48 +304,39 @@ void fa_bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sT[t] = Tr::mma(ka[s], qf[s], sT[t]);
-        pT[t] = Tr::mma(va[s], df[s], pT[t]);
+        sT = Tr::mma(ka[s], qf[s], sT);
+        pT = Tr::mma(va[s], df[s], pT);
       }
-    }
-    lds_mfma_pipeline<2 * NT * NS, 1, 6>();
-    const int jb = k0 + 4 * h;
-    const int hi = hi0 - jb, lo = lo0 - jb, sk = sk0 - jb;
-    v8 dsb[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
+      lds_mfma_pipeline<2 * NS, 1, 4>();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int e = 32 * t + 8 * (r >> 2) + (r & 3);
         float x;
         if (ALIBI)
-          x = __builtin_fmaf(sT[t][r], p.c, -b2 * fabsf((float)(i - jb - e))) - lse2;
+          x = __builtin_fmaf(sT[r], p.c, -b2 * fabsf((float)(i - jb - e))) - lse2;
         else
-          x = __builtin_fmaf(sT[t][r], p.c, -lse2);
+          x = __builtin_fmaf(sT[r], p.c, -lse2);
         float pr = fast_exp2(x);
         if (MASK) pr = ((e <= hi) & ((e >= lo) | (e <= sk))) ? pr : 0.f;
-        sT[t][r] = pr * (pT[t][r] - delta);   // dS^T
+        sT[r] = pr * (pT[r] - delta);   // dS^T
       }
-      dsb[t][0] = pack8<T>(sT[t], 0);
-      dsb[t][1] = pack8<T>(sT[t], 1);
-    }
-    // dQ^T += K^T dS^T
-    v8 kT[NT][2][NDT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
+      v8 dsb[2];
+      dsb[0] = pack8<T>(sT, 0);
+      dsb[1] = pack8<T>(sT, 1);
+      // dQ^T += K^T dS^T
+      v8 kT[2][NDT];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const T* kk = ks + (32 * t + 16 * u) * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) kT[t][u][dt] = lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]);
+        for (int dt = 0; dt < NDT; ++dt) kT[u][dt] = lds_tr8(kk + tro.lo[dt], kk + tro.hi[dt]);
       }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) dq[dt] = Tr::mma(kT[t][u][dt], dsb[t][u], dq[dt]);
-    lds_mfma_pipeline<2 * NT * NDT, 2, 4>();
+        for (int dt = 0; dt < NDT; ++dt) dq[dt] = Tr::mma(kT[u][dt], dsb[u], dq[dt]);
+      lds_mfma_pipeline<2 * NDT, 2, 2>();
+    }
     wait_vmem<0>();
     __syncthreads();
   };
