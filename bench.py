@@ -49,9 +49,9 @@ MEASURED_TRAFFIC = {
     # forward kernel, 4 waves: FETCH 388976.5 KiB, WRITE 66801.2 KiB per launch
     ("causal_b4h16s4096d128_bf16",
      "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 865027277,
-    # dq + dkv kernels: FETCH 394002.3 + 364194.8 KiB, WRITE 67585.2 + 131072 KiB per step
+    # dq + dkv kernels: FETCH 424169.0 + 364121.0 KiB, WRITE 67623.1 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "4c1e3d67e4c284c291c01f2157309aa63ce57058212b2ab78c9913bf4f1d0fe5"): 1756212429,
+     "60ee8613d808f5d5260dcf9f484b8fc80a56c5c2d0081157962ca6c14ad21e9d"): 1817881702,
     # forward kernel, f16 D=64: FETCH 3193.2 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
      "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 8702300,
