@@ -529,6 +529,39 @@ def test_backward_grouped_heads_alibi_scale(dtype):
     _bwd_case(1, 4, 2, 700, 128, dtype, True, 300, 4, 0.088, seed=8, label="gqa window")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_sharp_softmax(dtype):
+    """Q x 6: nearly one-hot probability rows, so P is recomputed from scores far
+    from the row max (exp2 arguments down to about -100) and dS is dominated by
+    a few keys per row."""
+    q, k, v = fa_inputs.make_qkv(1, 2, 300, 128, dtype, seed=21)
+    q6 = (q.float() * 6).to(q.dtype)
+    dout = fa_inputs.make_qkv(1, 2, 300, 128, dtype, seed=22)[0]
+    scale = 1.0 / math.sqrt(128)
+    qd, kd, vd = (t.cuda() for t in (q6, k, v))
+    o, lse = fa.flash_attn_fwd(qd, kd, vd, causal=True, scale=scale)
+    dq, dk, dv = fa.flash_attn_bwd(qd, kd, vd, o, lse, dout.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = ORACLE.attention_bwd(fa_inputs.to_f64(q6), fa_inputs.to_f64(k), fa_inputs.to_f64(v),
+                                      fa_inputs.to_f64(dout), causal=True, scale=scale)
+    errs = [_grad_err(dq, rq), _grad_err(dk, rk), _grad_err(dv, rv)]
+    _say(f"  {dtype} Qx6 backward: dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert max(errs) <= TOL_G[dtype], errs
+
+
+def test_split_keys_sharp_softmax():
+    """Key splits on nearly one-hot rows: partial LSEs of one row differ by tens,
+    and the merge must weight the partials by them (not average them)."""
+    q, k, v = fa_inputs.make_qkv(1, 2, 700, 128, "bf16", seed=23)
+    q8 = (q.float() * 8).to(q.dtype)
+    for n_split in (2, 5):
+        o, lse = fa.flash_attn_fwd_split(q8.cuda(), k.cuda(), v.cuda(), n_split=n_split,
+                                         causal=True, scale=1 / math.sqrt(128))
+        torch.cuda.synchronize()
+        compare(o, lse, q8, k, v, "bf16", causal=True, scale=1 / math.sqrt(128),
+                label=f"bf16 Qx8 split{n_split}")
+
+
 def test_backward_headline_shape_sampled():
     """The headline shape (B4 H16 S4096 D128 bf16 causal): two heads against
     the oracle, the rest finite."""
