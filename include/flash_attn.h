@@ -54,8 +54,9 @@ enum {
  *           type `dtype`, 16-byte aligned. Read only; they may alias each other.
  * o       : device pointer, [B, H, S, D], `dtype`, 16-byte aligned. Must not
  *           overlap q, k or v. Every element is written.
- * lse     : device pointer, [B, H, S] fp32, 4-byte aligned. Every element is
- *           written: the natural-log logsumexp of the scaled, masked score row.
+ * lse     : device pointer, [B, H, S] fp32, 4-byte aligned. Must not overlap
+ *           q, k, v or o. Every element is written: the natural-log
+ *           logsumexp of the scaled, masked score row.
  * B, H, S : >= 1.   D : head dimension, one of 16, 32, 64, 128.
  * causal  : 0 or 1.  window >= 0 (window > 0 needs causal == 1).  n_sink >= 0.
  * scale   : finite fp32 multiplier of Q.K (used as given: 0 and negative values
@@ -75,7 +76,8 @@ enum {
  *
  * Errors: FA_ERR_INVALID (NULL pointer, B/H/S < 1, causal not 0/1, window < 0,
  * window > 0 with causal == 0, n_sink < 0, non-finite scale, unknown dtype,
- * misaligned pointer, o overlapping q/k/v, byte sizes overflowing int64),
+ * misaligned pointer, o overlapping q/k/v, lse overlapping q/k/v/o, byte sizes
+ * overflowing int64),
  * FA_ERR_UNSUPPORTED (D not in {16,32,64,128}; S, B*H or the grid beyond the
  * 32-bit index range), FA_ERR_HIP (launch failure). On any error nothing is
  * enqueued and flash_attn_last_error() describes it.

@@ -86,8 +86,9 @@ int forward(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, kvbytes) ||
       overlaps(o, tbytes, v, kvbytes))
     return fail(FA_ERR_INVALID, "o overlaps q, k or v");
-  if (overlaps(lse, (uint64_t)rows * 4, o, tbytes))
-    return fail(FA_ERR_INVALID, "lse overlaps o");
+  if (overlaps(lse, (uint64_t)rows * 4, o, tbytes) || overlaps(lse, (uint64_t)rows * 4, q, tbytes) ||
+      overlaps(lse, (uint64_t)rows * 4, k, kvbytes) || overlaps(lse, (uint64_t)rows * 4, v, kvbytes))
+    return fail(FA_ERR_INVALID, "lse overlaps o, q, k or v");
   if (alibi && (overlaps(alibi, (uint64_t)H * 4, o, tbytes) ||
                 overlaps(alibi, (uint64_t)H * 4, lse, (uint64_t)rows * 4)))
     return fail(FA_ERR_INVALID, "alibi_slopes overlaps o or lse");

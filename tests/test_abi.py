@@ -103,6 +103,8 @@ INVALID = {
     "o_overlaps_q": dict(o=Q + 64),
     "o_overlaps_v": dict(o=V - 64),
     "lse_overlaps_o": dict(lse=O + 128),
+    "lse_overlaps_q": dict(lse=Q + 256),
+    "lse_overlaps_k": dict(lse=K),
     "size_overflow": dict(B=1 << 40, H=1 << 20, S=1 << 10),
     "counter_misaligned": dict(counter=0x600004),
 }
