@@ -47,9 +47,14 @@ template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float 
 }
 
 // max / sum of x[lane] and x[lane ^ 32] via v_permlane32_swap.
+// NaN-propagating maximum. Unlike fmaxf it needs no NaN-quieting copy of an
+// operand that is not known to be canonical (an MFMA result), and nested
+// pairs of it become single v_maximum3_f32 instructions.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -169,22 +169,22 @@ struct Core {
   // Online softmax with lazy rescale: turns the (masked) scores into p,
   // adds them to l and packs them into the B operands of the PV MFMA.
   __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2]) {
-    // Row max in four independent chains of three-input maxes, then joined:
-    // one chain of dependent maxes would sit on the path from the last QK
-    // MFMA to the first exponential.
-    float m4[4];
+    // Row max: one chain of three-input maxima per 32-key sub-tile, the
+    // first seeded with the running max (the lane pair holding a row shares
+    // it), then the exchange across the half-waves.
+    // Sub-tile 0: the running max and 16 scores (8 v_maximum3); later
+    // sub-tiles: 15 scores (7), their 16th joins the final maximum3.
+    float mj = vmax(vmax(m_run, acc[0][0]), acc[0][1]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float a = acc[0][k];
+    for (int r = 2; r < 16; r += 2) mj = vmax(vmax(mj, acc[0][r]), acc[0][r + 1]);
 #pragma unroll
-      for (int e = k + 4; e < 16 * NT; e += 8) {
-        const float x = acc[e >> 4][e & 15];
-        a = (e + 4 < 16 * NT) ? fmaxf(fmaxf(a, x), acc[(e + 4) >> 4][(e + 4) & 15]) : fmaxf(a, x);
-      }
-      m4[k] = a;
+    for (int t = 1; t < NT; ++t) {
+      float a = vmax(vmax(acc[t][0], acc[t][1]), acc[t][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) a = vmax(vmax(a, acc[t][r]), acc[t][r + 1]);
+      mj = vmax(vmax(mj, a), acc[t][15]);
     }
-    const float mt = xhalf_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = xhalf_max(mj);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + tau_raw)) {
       const float mc_new = (m_new == kNegInf) ? 0.f : m_new * c;
       const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
