@@ -46,15 +46,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
-    # forward kernel, 4 waves: FETCH 388976.5 KiB, WRITE 66801.2 KiB per launch
+    # forward kernel, 4 waves: FETCH 389588.0 KiB, WRITE 66857.9 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 865027277,
-    # dq + dkv kernels: FETCH 424169.0 + 364121.0 KiB, WRITE 67623.1 + 131072 KiB per step
+     "b86a2fbd4447ab326be8aa1e849777da5293ea2fb6e531785ef2b4889027e020"): 866338714,
+    # dq + dkv kernels: FETCH 417367.0 + 364146.0 KiB, WRITE 67617.1 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "60ee8613d808f5d5260dcf9f484b8fc80a56c5c2d0081157962ca6c14ad21e9d"): 1817881702,
-    # forward kernel, f16 D=64: FETCH 3193.2 KiB, WRITE 2112 KiB per launch
+     "169e272bddc6ccfec9921e714895c03416bd508aa61d1d99dbf7833e65178756"): 1803996262,
+    # forward kernel, f16 D=64: FETCH 3203.5 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
-     "4dbbd903abe125413c2f08b35d6bfdf67e5635f72a82b051cfeb5228f30bd519"): 8702300,
+     "b86a2fbd4447ab326be8aa1e849777da5293ea2fb6e531785ef2b4889027e020"): 8723456,
 }
 
 
