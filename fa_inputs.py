@@ -121,6 +121,22 @@ def make_qkv(B: int, H: int, S: int, D: int, dtype: str, seed: int = 0,
     return tuple(out)
 
 
+def make_qkv_device(S: int, D: int, dtype: str, seed: int, device) -> tuple:
+    """(q, k, v) of one head, [1, 1, S, D] in `dtype`, drawn N(0, 1) by torch's
+    generator on `device` (for sequences too long to draw on the host); rows
+    are drawn in chunks so the fp32 staging stays small."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(3):
+        t = torch.empty((1, 1, S, D), dtype=DTYPES[dtype], device=device)
+        for r0 in range(0, S, 1 << 20):
+            r1 = min(S, r0 + (1 << 20))
+            t[0, 0, r0:r1] = torch.randn((r1 - r0, D), generator=g, device=device).to(DTYPES[dtype])
+        out.append(t)
+    return tuple(out)
+
+
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.S, w.D, w.dtype, w.seed, w.lab3_draw, w.H_kv)
 

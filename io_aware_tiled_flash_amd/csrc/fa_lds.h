@@ -72,7 +72,9 @@ struct TileDma {
     const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g64);
     const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g64 >> 32));
     const uint64_t base = (((uint64_t)ghi << 32) | glo) + (uint64_t)(uint32_t)k0 * (D * sizeof(T));
-    const int bytes = (S - k0) * D * (int)sizeof(T);
+    // The descriptor covers this tile only (rows past the sequence end read
+    // as zero), so its 32-bit size cannot overflow however long S is.
+    const int bytes = min(S - k0, kBCf) * D * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>(base), (short)0, bytes, kBufferFlags);
 #pragma unroll

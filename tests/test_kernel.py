@@ -124,6 +124,52 @@ def test_workload_parity(name):
             assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0].repeat_interleave(G, dim=1))
 
 
+def test_sequence_longer_than_2_to_the_24():
+    """S = 2^24 + 77 keys of D = 128 bf16: one head's K is 4.3 GB, beyond a
+    32-bit byte count, so every tile load has to address it correctly. With a
+    96-key window and 3 sinks each row sees at most 99 keys, so the oracle
+    checks sampled rows on a compacted copy of the keys a row sees: the sinks
+    followed by its window, with the query last. The mask depends only on
+    i - j and on j < n_sink, so that row's visible set and its scores are the
+    same as in the long sequence."""
+    S, D, W, NS = (1 << 24) + 77, 128, 96, 3
+    scale = 1.0 / math.sqrt(D)
+    _say("long sequence: generating inputs on the device")
+    q, k, v = fa_inputs.make_qkv_device(S, D, "bf16", seed=11, device="cuda")
+    _say("long sequence: launching")
+    o, lse = fa.flash_attn_fwd(q, k, v, causal=True, window=W, n_sink=NS, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 2, 3, 97, 98, 99, 100, S // 2, S - 2, S - 1, (1 << 24) - 1, 1 << 24,
+                       (1 << 23) + 5]) | set(rng.integers(0, S, size=40).tolist()))
+    worst_o = worst_l = 0.0
+    for i in rows:
+        lo = max(NS, i - W + 1)
+        keys = list(range(min(NS, i + 1))) + list(range(lo, i + 1))
+        L = len(keys)
+        idx = torch.tensor(keys, device="cuda")
+        kc = k[0, 0].index_select(0, idx).cpu()
+        vc = v[0, 0].index_select(0, idx).cpu()
+        qc = torch.zeros((L, D), dtype=q.dtype)
+        qc[L - 1] = q[0, 0, i].cpu()
+        # compact positions: sinks 0..ns-1, then the window ending at L - 1
+        ns = min(NS, i + 1)
+        O, Lse = ORACLE.attention_fwd(fa_inputs.to_f64(qc.reshape(1, 1, L, D)),
+                                      fa_inputs.to_f64(kc.reshape(1, 1, L, D)),
+                                      fa_inputs.to_f64(vc.reshape(1, 1, L, D)), causal=True,
+                                      scale=scale, window=(L - ns) if i >= NS else 0,
+                                      n_sink=ns if i >= NS else 0, rows=[L - 1])
+        og = o[0, 0, i].float().cpu().double().numpy()
+        lg = float(lse[0, 0, i].cpu())
+        worst_o = max(worst_o, float(np.abs(og - O[0, 0, 0]).max()))
+        worst_l = max(worst_l, abs(lg - float(Lse[0, 0, 0])) / max(1.0, abs(float(Lse[0, 0, 0]))))
+    _say(f"  long sequence S={S}: max|dO|={worst_o:.3e}  max rel dLSE={worst_l:.3e}")
+    assert worst_o <= TOL_O["bf16"] and worst_l <= TOL_LSE_REL
+    assert torch.isfinite(lse).all()
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 # --------------------------------------------------------------------------- #
 # Ragged lengths, head dims, dtypes, masks
 # --------------------------------------------------------------------------- #
