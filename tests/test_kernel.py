@@ -170,6 +170,55 @@ def test_sequence_longer_than_2_to_the_24():
     torch.cuda.empty_cache()
 
 
+def test_hip_graph_capture_and_replay():
+    """Every call only enqueues kernels on the current stream (no allocation
+    with caller-provided buffers, no memset, no host synchronisation), so the
+    forward, the key-split forward with its merge, and the backward can be
+    captured into one HIP graph. Each replay, with eager work and
+    synchronisations in between, must equal the eager results bitwise."""
+    B, H, S, D = 2, 4, 700, 128
+    q, k, v = (t.cuda() for t in fa_inputs.make_qkv(B, H, S, D, "bf16", seed=21))
+    dout = fa_inputs.make_qkv(B, H, S, D, "bf16", seed=22)[0].cuda()
+    kw = dict(causal=True, window=300, n_sink=4)
+    o_ref, l_ref = fa.flash_attn_fwd(q, k, v, **kw)
+    os_ref, ls_ref = fa.flash_attn_fwd_split(q, k, v, n_split=3, **kw)
+    g_ref = fa.flash_attn_bwd(q, k, v, o_ref, l_ref, dout, **kw)
+    torch.cuda.synchronize()
+
+    o, os_, dq, dk, dv = (torch.empty_like(q) for _ in range(5))
+    l, ls_ = (torch.empty((B, H, S), dtype=torch.float32, device="cuda") for _ in range(2))
+    ws_split = torch.empty(fa.flash_attn_split_workspace_bytes(B, H, S, D, 3), dtype=torch.uint8,
+                           device="cuda")
+    ws_bwd = torch.empty(fa.flash_attn_bwd_workspace_bytes(B, H, S), dtype=torch.uint8,
+                         device="cuda")
+
+    def calls():
+        fa.flash_attn_fwd(q, k, v, out=o, lse=l, **kw)
+        fa.flash_attn_fwd_split(q, k, v, n_split=3, workspace=ws_split, out=os_, lse=ls_, **kw)
+        fa.flash_attn_bwd(q, k, v, o, l, dout, workspace=ws_bwd, dq=dq, dk=dk, dv=dv, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                                   # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    outs = (o, l, os_, ls_, dq, dk, dv)
+    refs = (o_ref, l_ref, os_ref, ls_ref) + tuple(g_ref)
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))                 # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("o", "lse", "o split", "lse split", "dq", "dk", "dv"), outs, refs):
+            assert torch.equal(t, r), (rep, name)
+    _say("  graph: 4 replays bitwise equal to the eager calls")
+
+
 # --------------------------------------------------------------------------- #
 # Ragged lengths, head dims, dtypes, masks
 # --------------------------------------------------------------------------- #
