@@ -110,6 +110,19 @@ __device__ __forceinline__ bool block_full(int q_lo, int k0, int S, int causal, 
   return full;
 }
 
+// True when no key of the block [k0, k0 + BC) is visible to any of the query
+// rows [r0, r1]: past the rows under the causal mask, or wholly before every
+// row's window and holding no sink. The diagonal block of a 128-row query block
+// is like this for the waves of its upper rows.
+template <int BC>
+__device__ __forceinline__ bool block_hidden(int r0, int r1, int k0, int causal, int window,
+                                             int n_sink) {
+  if (!causal) return false;
+  if (k0 > r1) return true;
+  const int k1 = k0 + BC - 1;
+  return window > 0 && k0 >= n_sink && k1 < r0 && r0 - k1 >= window;
+}
+
 // Work-group -> (query block, batch*head). Heaviest query blocks first under
 // the causal mask. Consecutive ids walk over heads, and the dispatcher deals
 // ids round-robin over the 8 XCDs, so with B*H a multiple of 8 every query

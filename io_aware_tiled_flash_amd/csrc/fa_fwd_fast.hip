@@ -361,13 +361,20 @@ void fa_fwd_fast_kernel(FwdParams p) {
       kdma.load(kn, Kh, k1, S, wave);
       vdma.load(vn, Vh, k1, S, wave);
     }
-    f32x16 sacc[C::NT];
-    core.qk(sacc, kc);
-    if (decltype(mask)::value) core.mask(sacc, p, kb(it) * BC);
-    if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, kb(it) * BC + 4 * core.h);
-    typename C::v8 pb[C::NT][2];
-    core.softmax(sacc, pb);
-    core.pv(vc, pb);
+    // In a partially visible block, a wave whose 32 rows see none of its keys
+    // (above the causal diagonal, or before the window) skips the block.
+    const int k0 = kb(it) * BC;
+    if (!decltype(mask)::value ||
+        !block_hidden<BC>(q_lo + 32 * wave, q_lo + 32 * wave + 31, k0, p.causal, p.window,
+                          p.n_sink)) {
+      f32x16 sacc[C::NT];
+      core.qk(sacc, kc);
+      if (decltype(mask)::value) core.mask(sacc, p, k0);
+      if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
+      typename C::v8 pb[C::NT][2];
+      core.softmax(sacc, pb);
+      core.pv(vc, pb);
+    }
     wait_vmem<0>();
     __syncthreads();
   };
