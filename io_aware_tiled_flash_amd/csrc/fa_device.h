@@ -168,6 +168,24 @@ __device__ __forceinline__ void alibi_logits(f32x16 (&acc)[NT], float c, float b
     }
 }
 
+// The ALiBi bias in raw score units (base-2 logit / c) under the causal mask,
+// where j <= i for every visible key: -beta |i - j| = beta (j - i), with
+// beta = slope log2(e) / c and key j = jb + 4h + e. This adds the per-key part beta e (e a compile-time
+// constant, one FMA per score); the per-row part beta (jb + 4h - i) is one
+// number per lane and block, applied in the softmax.
+template <int NT>
+__device__ __forceinline__ void alibi_ramp(f32x16 (&acc)[NT], float beta) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[t][r] = __builtin_fmaf((float)(32 * t + 8 * (r >> 2) + (r & 3)), beta, acc[t][r]);
+}
+
+// Smallest softmax scale (|scale| log2 e) for which the linear ALiBi form is
+// used: beta = slope log2(e) / c stays far from overflow.
+constexpr float kAlibiMinScale = 1e-6f;
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace fa

@@ -54,7 +54,7 @@ namespace {
 // owns 32 query rows; lane (col, h) = (lane & 31, lane >> 5) owns query row
 // i = q_lo + 32 * wave_in_block + col and, in every 32-key sub-tile, the keys
 // 8 g + 4 h + r (g, r < 4) of the S^T accumulator.
-template <typename T, int D, int BR, bool ALIBI>
+template <typename T, int D, int BR, int AL>
 struct Core {
   using Tr = Half16<T>;
   using v8 = typename Tr::v8;
@@ -71,12 +71,13 @@ struct Core {
   float mc;          // m_run * c, or 0 while nothing is visible
   float l[4];        // this lane half's running sum, in 4 parts
   float c, tau_raw;  // softmax scale (1 when ALiBi logits are already scaled)
-  float b2;          // ALiBi slope in base 2 (ALIBI only)
+  float b2;          // ALiBi slope in base 2 (AL != 0)
+  float beta;        // b2 / c: the ALiBi slope in raw score units (AL == 1)
   int i, h, col;
 
   __device__ __forceinline__ void init(const FwdParams& p, const T* __restrict__ Qh, int q_row,
                                        int lane, int bh) {
-    b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
+    b2 = AL ? p.alibi[bh % p.H] * kLog2e : 0.f;
     h = lane >> 5;
     col = lane & 31;
     i = q_row;
@@ -104,7 +105,8 @@ struct Core {
     mc = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) l[k] = 0.f;
-    c = ALIBI ? 1.f : p.c;
+    c = (AL == 2) ? 1.f : p.c;
+    beta = (AL == 1) ? b2 / p.c : 0.f;
     tau_raw = kTau / c;
   }
 
@@ -168,13 +170,16 @@ struct Core {
 
   // Online softmax with lazy rescale: turns the (masked) scores into p,
   // adds them to l and packs them into the B operands of the PV MFMA.
-  __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2]) {
+  // off (AL == 1 only): this lane's ALiBi offset for the block, added to
+  // every score the lane holds after the per-key ramp (see alibi_ramp).
+  __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2], float off = 0.f) {
     // Row max: one chain of three-input maxima per 32-key sub-tile, the
     // first seeded with the running max (the lane pair holding a row shares
     // it), then the exchange across the half-waves.
     // Sub-tile 0: the running max and 16 scores (8 v_maximum3); later
-    // sub-tiles: 15 scores (7), their 16th joins the final maximum3.
-    float mj = vmax(vmax(m_run, acc[0][0]), acc[0][1]);
+    // sub-tiles: 15 scores (7), their 16th joins the final maximum3. With
+    // the ALiBi offset the running max joins after the offset is added.
+    float mj = (AL == 1) ? vmax(acc[0][0], acc[0][1]) : vmax(vmax(m_run, acc[0][0]), acc[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mj = vmax(vmax(mj, acc[0][r]), acc[0][r + 1]);
 #pragma unroll
@@ -184,7 +189,8 @@ struct Core {
       for (int r = 3; r < 15; r += 2) a = vmax(vmax(a, acc[t][r]), acc[t][r + 1]);
       mj = vmax(vmax(mj, a), acc[t][15]);
     }
-    const float m_new = xhalf_max(mj);
+    // (each half-wave adds its own offset, 4 beta apart, before the exchange)
+    const float m_new = (AL == 1) ? vmax(m_run, xhalf_max(mj + off)) : xhalf_max(mj);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + tau_raw)) {
       const float mc_new = (m_new == kNegInf) ? 0.f : m_new * c;
       const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
@@ -197,11 +203,12 @@ struct Core {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+    const float bo = (AL == 1) ? __builtin_fmaf(off, c, -mc) : -mc;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(acc[t][r], c, -mc));
+        const float e = fast_exp2(__builtin_fmaf(acc[t][r], c, bo));
         acc[t][r] = e;
         l[r & 3] += e;
       }
@@ -289,12 +296,12 @@ struct Core {
 // being read and does not wait for the in-flight loads before each read (it
 // would have to if both were slots of one array picked at run time).
 // ------------------------------------------------------------------------ //
-template <typename T, int D, int NW, bool ALIBI>
+template <typename T, int D, int NW, int AL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fast_kernel(FwdParams p) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kBCf;
-  using C = Core<T, D, BR, ALIBI>;
+  using C = Core<T, D, BR, AL>;
   constexpr int TILE = BC * D;
 
   __shared__ __attribute__((aligned(1024))) T k0s[TILE];
@@ -318,15 +325,23 @@ void fa_fwd_fast_kernel(FwdParams p) {
   const size_t head = (size_t)bh * (size_t)S * D;
   const size_t kv_head = (size_t)(bh / p.G) * (size_t)S * D;
   const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + kv_head;
+  // K/V head bases are wave-uniform; moved to scalar registers once here, the
+  // per-block descriptor arithmetic of the tile loads stays scalar.
+  const T* __restrict__ Kh = uniform_ptr(reinterpret_cast<const T*>(p.k) + kv_head);
+  const T* __restrict__ Vh = uniform_ptr(reinterpret_cast<const T*>(p.v) + kv_head);
 
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_all = br.count();
   const int it_b = (int)((int64_t)split * n_all / p.n_split);
   const int n_iter = (int)((int64_t)(split + 1) * n_all / p.n_split) - it_b;
-  // key block of the t-th step of this work-group
-  auto kb = [&](int t) __attribute__((always_inline)) { return br.kb(it_b + t); };
+  // key block of the t-th step of this work-group. With ALiBi under the
+  // causal mask the walk runs backwards, from the diagonal: the bias only
+  // falls with distance, so the first blocks hold the row maximum and the
+  // running max seldom moves afterwards (forwards, it would move, and O be
+  // rescaled, at nearly every block of the steeper heads).
+  auto kb = [&](int t) __attribute__((always_inline)) {
+    return br.kb(it_b + (AL == 1 ? n_iter - 1 - t : t));
+  };
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_iter);
 
   TileDma<T, D, NW, false> kdma;
@@ -370,9 +385,10 @@ void fa_fwd_fast_kernel(FwdParams p) {
       f32x16 sacc[C::NT];
       core.qk(sacc, kc);
       if (decltype(mask)::value) core.mask(sacc, p, k0);
-      if (ALIBI) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
+      if (AL == 2) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
+      if (AL == 1) alibi_ramp<C::NT>(sacc, core.beta);
       typename C::v8 pb[C::NT][2];
-      core.softmax(sacc, pb);
+      core.softmax(sacc, pb, AL == 1 ? core.beta * (float)(k0 + 4 * core.h - core.i) : 0.f);
       core.pv(vc, pb);
     }
     wait_vmem<0>();
@@ -414,9 +430,10 @@ int fast_tile_keys() { return kBCf; }
 // Explicit instantiations: with several instantiations of the kernel template
 // in one translation unit, the host pass emitted launch stubs only for the
 // first boolean variant it met; naming each one here makes all of them exist.
-#define FA_FAST_INST(T, D, NW)                                             \
-  template __global__ void fa_fwd_fast_kernel<T, D, NW, false>(FwdParams); \
-  template __global__ void fa_fwd_fast_kernel<T, D, NW, true>(FwdParams);
+#define FA_FAST_INST(T, D, NW)                                         \
+  template __global__ void fa_fwd_fast_kernel<T, D, NW, 0>(FwdParams); \
+  template __global__ void fa_fwd_fast_kernel<T, D, NW, 1>(FwdParams); \
+  template __global__ void fa_fwd_fast_kernel<T, D, NW, 2>(FwdParams);
 FA_FAST_INST(__bf16, 128, 8)
 FA_FAST_INST(__bf16, 128, 4)
 FA_FAST_INST(__bf16, 64, 8)
@@ -427,21 +444,28 @@ FA_FAST_INST(_Float16, 64, 8)
 FA_FAST_INST(_Float16, 64, 4)
 #undef FA_FAST_INST
 
-template <typename T, int D, bool ALIBI>
+template <typename T, int D, int AL>
 static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH * (unsigned)p.n_split;
   if (nw == 8)
-    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, ALIBI>), dim3(grid), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, AL>), dim3(grid), dim3(512), 0, st, p);
   else
-    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 4, ALIBI>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 4, AL>), dim3(grid), dim3(256), 0, st, p);
 }
 
+// ALiBi variants: under the causal mask every visible key has j <= i, so the
+// bias -slope |i - j| = slope (j - i) is linear in the key and costs one FMA
+// per score (AL = 1). Without the mask, or with a scale so small that
+// slope / scale would not be a usable number, the bias is formed per score
+// with its absolute value (AL = 2).
 template <typename T, int D>
 static hipError_t launch_fast_t(const FwdParams& p, int nw, hipStream_t st) {
-  if (p.alibi)
-    launch_fast_a<T, D, true>(p, nw, st);
+  if (!p.alibi)
+    launch_fast_a<T, D, 0>(p, nw, st);
+  else if (p.causal && p.c >= kAlibiMinScale)
+    launch_fast_a<T, D, 1>(p, nw, st);
   else
-    launch_fast_a<T, D, false>(p, nw, st);
+    launch_fast_a<T, D, 2>(p, nw, st);
   return hipGetLastError();
 }
 

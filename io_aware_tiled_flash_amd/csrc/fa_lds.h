@@ -84,6 +84,15 @@ struct TileDma {
   }
 };
 
+// A wave-uniform pointer moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (gfx9 encoding:
 // vmcnt low bits [3:0], high bits [15:14]).
 template <int N>
