@@ -46,15 +46,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
-    # forward kernel, 4 waves: FETCH 389588.0 KiB, WRITE 66857.9 KiB per launch
+    # forward kernel, 4 waves: FETCH 413826.0 KiB, WRITE 69356.4 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "b86a2fbd4447ab326be8aa1e849777da5293ea2fb6e531785ef2b4889027e020"): 866338714,
-    # dq + dkv kernels: FETCH 417367.0 + 364146.0 KiB, WRITE 67617.1 + 131072 KiB per step
+     "b36e261f9c748814bd37d461264fa8f78a08f8d43a2171bf5ee866eacc3387ec"): 918536602,
+    # dq + dkv kernels: FETCH 430615.0 + 364174.0 KiB, WRITE 67691.8 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "169e272bddc6ccfec9921e714895c03416bd508aa61d1d99dbf7833e65178756"): 1803996262,
-    # forward kernel, f16 D=64: FETCH 3203.5 KiB, WRITE 2112 KiB per launch
+     "e5a1c745403c7bb4004b10987d03221fb2093aac47cd61f4eab1d27be598f93a"): 1831262003,
+    # forward kernel, f16 D=64: FETCH 3205.9 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
-     "b86a2fbd4447ab326be8aa1e849777da5293ea2fb6e531785ef2b4889027e020"): 8723456,
+     "b36e261f9c748814bd37d461264fa8f78a08f8d43a2171bf5ee866eacc3387ec"): 8728474,
 }
 
 
