@@ -185,6 +185,11 @@ __device__ __forceinline__ void alibi_ramp(f32x16 (&acc)[NT], float beta) {
 // Smallest softmax scale (|scale| log2 e) for which the linear ALiBi form is
 // used: beta = slope log2(e) / c stays far from overflow.
 constexpr float kAlibiMinScale = 1e-6f;
+// Largest |slope log2 e| for the linear form: the ramp and offset then stay
+// below 16 * 2^8 log2 units in the blocks that carry the row's weight, so
+// the scores keep all but a few of their bits (the error in an exponent is
+// about 2^-24 of that size).
+constexpr float kAlibiLinMaxB2 = 16.f;
 
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -297,17 +297,10 @@ struct Core {
 // would have to if both were slots of one array picked at run time).
 // ------------------------------------------------------------------------ //
 template <typename T, int D, int NW, int AL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_fast_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* k1s, T* v1s) {
   constexpr int BR = 32 * NW;
   constexpr int BC = kBCf;
   using C = Core<T, D, BR, AL>;
-  constexpr int TILE = BC * D;
-
-  __shared__ __attribute__((aligned(1024))) T k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) T v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) T k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) T v1s[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -417,6 +410,30 @@ void fa_fwd_fast_kernel(FwdParams p) {
     core.epilogue_partial(p, split, bh);
   else
     core.epilogue(p, head, bh);
+}
+
+template <typename T, int D, int NW, int AL>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_fast_kernel(FwdParams p) {
+  constexpr int TILE = kBCf * D;
+  __shared__ __attribute__((aligned(1024))) T k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v1s[TILE];
+  if constexpr (AL == 1) {
+    // The linear ALiBi form adds the bias as beta (j - i) in parts of size up
+    // to beta * 64 and more; for steep slopes those parts would swamp the
+    // score's own bits, so such heads take the per-score |i - j| form.
+    const int per = p.nqb * p.BH;
+    int qb, bh;
+    wg_coords(p, (int)blockIdx.x % per, qb, bh);
+    if (fabsf(p.alibi[bh % p.H] * kLog2e) <= kAlibiLinMaxB2)
+      fwd_body<T, D, NW, 1>(p, k0s, v0s, k1s, v1s);
+    else
+      fwd_body<T, D, NW, 2>(p, k0s, v0s, k1s, v1s);
+  } else {
+    fwd_body<T, D, NW, AL>(p, k0s, v0s, k1s, v1s);
+  }
 }
 
 // ------------------------------------------------------------------------ //

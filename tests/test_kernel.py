@@ -458,6 +458,24 @@ def test_alibi_negative_scale_and_zero_scale():
                     alibi=sl.astype(np.float64), label=f"alibi scale {scale} c{int(causal)}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_alibi_slope_range_causal(dtype):
+    """Under the causal mask the fast kernel adds the bias in a linear form for
+    moderate slopes and per score for steep ones (|slope log2 e| > 16): slopes
+    on both sides of that switch, negative and very large ones, with the
+    reversed block walk, a ragged tail and a window."""
+    H = 8
+    sl = np.array([0.5, -0.3, 11.0, 11.2, 40.0, 1e3, 1e30, -2.0], dtype=np.float32)
+    sd = torch.from_numpy(sl).cuda()
+    for S, window, n_sink in ((333, 0, 0), (700, 150, 3)):
+        q, k, v = fa_inputs.make_qkv(1, H, S, 128, dtype, seed=S + 40)
+        scale = 1.0 / math.sqrt(128)
+        o, lse = gpu_fwd(q, k, v, causal=True, window=window, n_sink=n_sink, scale=scale,
+                         alibi_slopes=sd)
+        compare(o, lse, q, k, v, dtype, causal=True, scale=scale, window=window, n_sink=n_sink,
+                alibi=sl.astype(np.float64), label=f"{dtype} S{S} w{window} alibi slope range")
+
+
 def test_alibi_rejects_bad_slopes_tensor():
     q, k, v = (t.cuda() for t in fa_inputs.make_qkv(1, 4, 64, 64, "bf16", seed=1))
     with pytest.raises(ValueError):
