@@ -46,15 +46,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
-    # forward kernel, 4 waves: FETCH 413826.0 KiB, WRITE 69356.4 KiB per launch
+    # forward kernel, 4 waves: FETCH 389947.0 KiB, WRITE 66858.9 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "b36e261f9c748814bd37d461264fa8f78a08f8d43a2171bf5ee866eacc3387ec"): 918536602,
-    # dq + dkv kernels: FETCH 430615.0 + 364174.0 KiB, WRITE 67691.8 + 131072 KiB per step
+     "08b201d58d0bdf24956e86e671817a7e103877100016e8ec42b605bdfb9b4bf6"): 867074970,
+    # dq + dkv kernels: FETCH 431403.0 + 364181.0 KiB, WRITE 67615.7 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "e5a1c745403c7bb4004b10987d03221fb2093aac47cd61f4eab1d27be598f93a"): 1831262003,
-    # forward kernel, f16 D=64: FETCH 3205.9 KiB, WRITE 2112 KiB per launch
+     "4110db48be30abe01f301e2ad433837f950d1024fd44b9951ad9d057eb10bd65"): 1832812237,
+    # forward kernel, f16 D=64: FETCH 3204.7 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
-     "b36e261f9c748814bd37d461264fa8f78a08f8d43a2171bf5ee866eacc3387ec"): 8728474,
+     "08b201d58d0bdf24956e86e671817a7e103877100016e8ec42b605bdfb9b4bf6"): 8725893,
 }
 
 

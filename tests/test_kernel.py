@@ -219,6 +219,44 @@ def test_hip_graph_capture_and_replay():
     _say("  graph: 4 replays bitwise equal to the eager calls")
 
 
+def test_random_configurations():
+    """A seeded sweep over combinations the targeted tests cover one at a time:
+    batch, query and K/V heads, ragged S, D, dtype, mask (none, causal, window,
+    sinks), ALiBi, the sign and size of the scale, and plain vs key-split
+    forward. Each is checked against the oracle on every row."""
+    rng = np.random.default_rng(2024)
+    for n in range(36):
+        dtype = ["bf16", "f16", "f32"][n % 3]
+        D = int(rng.choice([16, 32, 64, 128])) if dtype == "f32" else int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 3]))
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 520))
+        causal = bool(rng.integers(0, 4) > 0)
+        window = int(rng.integers(1, 300)) if causal and rng.random() < 0.5 else 0
+        n_sink = int(rng.integers(0, 9)) if window else 0
+        scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.02, 0.3))
+        slopes = rng.uniform(-0.5, 1.5, size=H).astype(np.float32) if rng.random() < 0.4 else None
+        split = int(rng.integers(2, 5)) if dtype != "f32" and rng.random() < 0.3 else 0
+        q, _, _ = fa_inputs.make_qkv(B, H, S, D, dtype, seed=1000 + n)
+        k, v = _kv(B, Hkv, S, D, dtype, seed=2000 + n)
+        sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+        kw = dict(causal=causal, window=window, n_sink=n_sink, scale=scale, alibi_slopes=sd)
+        label = (f"#{n} {dtype} B{B} H{H}/{Hkv} S{S} D{D} c{int(causal)} w{window} s{n_sink} "
+                 f"scale {scale:+.3f} alibi {slopes is not None} split {split}")
+        if split:
+            o, lse = fa.flash_attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), n_split=split, **kw)
+            torch.cuda.synchronize()
+        else:
+            o, lse = gpu_fwd(q, k, v, **kw)
+        # fp32 rounding of the scores grows with their size: scale the fp32 bar
+        # by |scale| sqrt(D), which is 1 at the usual 1/sqrt(D)
+        tol = TOL_O["f32"] * max(1.0, abs(scale) * math.sqrt(D)) if dtype == "f32" else None
+        compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                n_sink=n_sink, label=label, tol_o=tol,
+                alibi=None if slopes is None else slopes.astype(np.float64))
+
+
 # --------------------------------------------------------------------------- #
 # Ragged lengths, head dims, dtypes, masks
 # --------------------------------------------------------------------------- #
