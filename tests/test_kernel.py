@@ -235,7 +235,10 @@ def test_random_configurations():
         causal = bool(rng.integers(0, 4) > 0)
         window = int(rng.integers(1, 300)) if causal and rng.random() < 0.5 else 0
         n_sink = int(rng.integers(0, 9)) if window else 0
-        scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.02, 0.3))
+        # within 1.5x of the usual 1/sqrt(D): sharper rows put |O| near the largest
+        # |v|, where rounding O to bf16 alone approaches the bf16 bar (the sharp
+        # softmax tests cover that regime with their own inputs)
+        scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.1, 1.5) / math.sqrt(D))
         slopes = rng.uniform(-0.5, 1.5, size=H).astype(np.float32) if rng.random() < 0.4 else None
         split = int(rng.integers(2, 5)) if dtype != "f32" and rng.random() < 0.3 else 0
         q, _, _ = fa_inputs.make_qkv(B, H, S, D, dtype, seed=1000 + n)
