@@ -668,6 +668,29 @@ def test_backward(dtype, D):
                       seed=S + D, label=f"{dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
 
 
+def test_backward_random_configurations():
+    """A seeded sweep of the backward over batch, grouped heads, ragged S, D,
+    dtype, mask, ALiBi and the scale's sign, each against the oracle's
+    gradients."""
+    rng = np.random.default_rng(77)
+    for n in range(14):
+        dtype = ["bf16", "f16"][n % 2]
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 300))
+        causal = bool(rng.integers(0, 4) > 0)
+        window = int(rng.integers(1, 200)) if causal and rng.random() < 0.5 else 0
+        n_sink = int(rng.integers(0, 6)) if window else 0
+        scale = float(rng.choice([1.0, -1.0]) * rng.uniform(0.3, 1.5) / math.sqrt(D))
+        slopes = rng.uniform(-0.3, 1.2, size=H) if rng.random() < 0.4 else None
+        _bwd_case(B, H, Hkv, S, D, dtype, causal, window, n_sink, scale, seed=5000 + 10 * n,
+                  slopes=slopes,
+                  label=f"#{n} {dtype} B{B} H{H}/{Hkv} S{S} D{D} c{int(causal)} w{window} "
+                        f"s{n_sink} scale {scale:+.3f} alibi {slopes is not None}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_backward_grouped_heads_alibi_scale(dtype):
     """Grouped K/V heads (dk, dv sum over the group), ALiBi, negative and zero
