@@ -48,13 +48,13 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
 MEASURED_TRAFFIC = {
     # forward kernel, 4 waves: FETCH 389947.0 KiB, WRITE 66858.9 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "08b201d58d0bdf24956e86e671817a7e103877100016e8ec42b605bdfb9b4bf6"): 867074970,
+     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 867074970,
     # dq + dkv kernels: FETCH 431403.0 + 364181.0 KiB, WRITE 67615.7 + 131072 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
      "4110db48be30abe01f301e2ad433837f950d1024fd44b9951ad9d057eb10bd65"): 1832812237,
     # forward kernel, f16 D=64: FETCH 3204.7 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
-     "08b201d58d0bdf24956e86e671817a7e103877100016e8ec42b605bdfb9b4bf6"): 8725893,
+     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 8725893,
 }
 
 

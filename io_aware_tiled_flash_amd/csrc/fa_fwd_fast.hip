@@ -35,7 +35,11 @@
 //    bounds and compile-time key offsets (two VALU ops per score). The
 //    partially visible blocks sit at the two ends of the visiting order, so
 //    the loop runs in three segments and only the end segments carry mask
-//    code.
+//    code. In those blocks a wave whose rows see none of the keys skips them.
+//  * ALiBi (template AL): under the causal mask the bias is linear in the key
+//    (AL == 1): one FMA with a compile-time ramp per score and one offset per
+//    lane and block, with the block walk running from the diagonal. Without
+//    the mask, or for steep slopes, the bias is formed per score (AL == 2).
 //
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,7 +74,7 @@ struct Core {
   float m_run;       // running max (raw sign-folded score units)
   float mc;          // m_run * c, or 0 while nothing is visible
   float l[4];        // this lane half's running sum, in 4 parts
-  float c, tau_raw;  // softmax scale (1 when ALiBi logits are already scaled)
+  float c, tau_raw;  // softmax scale (1 for AL == 2, whose logits come scaled)
   float b2;          // ALiBi slope in base 2 (AL != 0)
   float beta;        // b2 / c: the ALiBi slope in raw score units (AL == 1)
   int i, h, col;
