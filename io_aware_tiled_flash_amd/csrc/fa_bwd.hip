@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(
 void fa_bwd_dkv_kernel(BwdParams p) {
   constexpr int NW = kBwdWaves;
   constexpr int BK = 32 * NW;    // keys per work-group
-  constexpr int BQ = kBCf;       // query rows per streamed block
+  constexpr int BQ = 2 * kBCf;   // query rows per streamed block (two tile loads)
   constexpr int NT = BQ / 32;
   constexpr int NS = D / 16;
   constexpr int NDT = D / 32;
@@ -445,6 +445,13 @@ void fa_bwd_dkv_kernel(BwdParams p) {
     Qh = reinterpret_cast<const T*>(p.q) + head;
     dOh = reinterpret_cast<const T*>(p.dout) + head;
   };
+  // a BQ-row tile as kBCf-row loads; a part wholly past the sequence end
+  // loads row S - 1 and zeros (finite data; those rows carry P = 0)
+  auto tile_load = [&](T* dst, const T* src, int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BQ / kBCf; ++u)
+      dma.load(dst + u * kBCf * D, src, min(q0 + u * kBCf, S - 1), S, wave);
+  };
   auto block_full_kv = [&](int q0) __attribute__((always_inline)) {
     bool full = true;
     if (p.causal) {
@@ -459,16 +466,19 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   auto rows_dma = [&](float* dst, int bh, int q0) __attribute__((always_inline)) {
     if (wave == 0) {
       const size_t rb = (size_t)bh * p.Sp + q0;
-      rows_to_lds(dst, p.lse2 + rb, lane);
-      rows_to_lds(dst + BQ, p.delta + rb, lane);
+#pragma unroll
+      for (int u = 0; u < BQ / 64; ++u) {
+        rows_to_lds(dst + 64 * u, p.lse2 + rb + 64 * u, lane);
+        rows_to_lds(dst + BQ + 64 * u, p.delta + rb + 64 * u, lane);
+      }
     }
   };
   if (n_iter > 0) {
     const T *Qh, *dOh;
     int bh0, q00;
     tile_src(0, Qh, dOh, bh0, q00);
-    dma.load(q0s, Qh, q00, S, wave);
-    dma.load(d0s, dOh, q00, S, wave);
+    tile_load(q0s, Qh, q00);
+    tile_load(d0s, dOh, q00);
     rows_dma(r0s, bh0, q00);
   }
   wait_vmem<0>();
@@ -486,8 +496,8 @@ void fa_bwd_dkv_kernel(BwdParams p) {
       const T *Qn, *dOn;
       int bhn, qn;
       tile_src(it + 1, Qn, dOn, bhn, qn);
-      dma.load(PAR == 0 ? q1s : q0s, Qn, qn, S, wave);
-      dma.load(PAR == 0 ? d1s : d0s, dOn, qn, S, wave);
+      tile_load(PAR == 0 ? q1s : q0s, Qn, qn);
+      tile_load(PAR == 0 ? d1s : d0s, dOn, qn);
       rows_dma(PAR == 0 ? r1s : r0s, bhn, qn);
     }
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
