@@ -46,15 +46,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_kernel.h",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC = {
-    # forward kernel, 4 waves: FETCH 389947.0 KiB, WRITE 66858.9 KiB per launch
+    # forward kernel, 4 waves: FETCH 389972.4 KiB, WRITE 66878.1 KiB per launch
     ("causal_b4h16s4096d128_bf16",
-     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 867074970,
-    # dq + dkv kernels: FETCH 435388.0 + 364388.0 KiB, WRITE 67623.8 + 131072 KiB per step
+     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 867146650,
+    # dq + dkv kernels: FETCH 428291.4 + 364639.4 KiB, WRITE 67618.7 + 131072.3 KiB per step
     ("bwd_causal_b4h16s4096d128_bf16",
-     "86faa674d37e18ea9f12a83052f8d7abcf34ed54ba35d0139e6681acc98fa52f"): 1841405747,
-    # forward kernel, f16 D=64: FETCH 3204.7 KiB, WRITE 2112 KiB per launch
+     "86faa674d37e18ea9f12a83052f8d7abcf34ed54ba35d0139e6681acc98fa52f"): 1827381862,
+    # forward kernel, f16 D=64: FETCH 3204.8 KiB, WRITE 2112 KiB per launch
     ("noncausal_b2h8s1024d64_f16",
-     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 8725893,
+     "1f643d292e14bd72dd1eea47422a89db1e7a702035ffeb313375880610382494"): 8726118,
 }
 
 
