@@ -517,6 +517,35 @@ def test_alibi_slope_range_causal(dtype):
                 alibi=sl.astype(np.float64), label=f"{dtype} S{S} w{window} alibi slope range")
 
 
+def test_eight_wave_work_groups():
+    """The 8-wave (256-row) work-groups that long sequences use, forced on
+    shorter ones: ALiBi under the causal mask (backward walk), a window with
+    sinks, grouped heads and a ragged tail."""
+    old = os.environ.get("FLASH_ATTN_WAVES")
+    os.environ["FLASH_ATTN_WAVES"] = "8"
+    try:
+        H = 4
+        sl = np.array(list(ORACLE.alibi_slopes(H)), dtype=np.float32)
+        sd = torch.from_numpy(sl).cuda()
+        for dtype, D, S, Hkv, window, n_sink, al in (("bf16", 128, 611, 4, 0, 0, True),
+                                                    ("f16", 128, 700, 2, 200, 4, False),
+                                                    ("bf16", 64, 530, 1, 0, 0, False),
+                                                    ("f16", 64, 333, 2, 90, 3, True)):
+            q, _, _ = fa_inputs.make_qkv(1, H, S, D, dtype, seed=S + 3)
+            k, v = _kv(1, Hkv, S, D, dtype, seed=S + 4)
+            scale = 1.0 / math.sqrt(D)
+            o, lse = gpu_fwd(q, k, v, causal=True, window=window, n_sink=n_sink, scale=scale,
+                             alibi_slopes=sd if al else None)
+            compare(o, lse, q, k, v, dtype, causal=True, scale=scale, window=window,
+                    n_sink=n_sink, alibi=sl.astype(np.float64) if al else None,
+                    label=f"8 waves {dtype} D{D} S{S} Hkv{Hkv} w{window} alibi {al}")
+    finally:
+        if old is None:
+            del os.environ["FLASH_ATTN_WAVES"]
+        else:
+            os.environ["FLASH_ATTN_WAVES"] = old
+
+
 def test_alibi_rejects_bad_slopes_tensor():
     q, k, v = (t.cuda() for t in fa_inputs.make_qkv(1, 4, 64, 64, "bf16", seed=1))
     with pytest.raises(ValueError):
