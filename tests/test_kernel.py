@@ -720,6 +720,53 @@ def test_backward_random_configurations():
                         f"s{n_sink} scale {scale:+.3f} alibi {slopes is not None}")
 
 
+def test_backward_sequence_longer_than_2_to_the_24():
+    """The backward on one head of S = 2^24 + 77 keys (4.3 GB per tensor) with a
+    64-key window, checked on sampled rows against the oracle run on compact
+    copies: dQ of row i needs only keys [i - W + 1, i]; dK and dV of key j need
+    only the queries [j, j + W - 1], whose windows lie within [j - W + 1,
+    j + W - 1]. The mask depends on i - j alone, so the compact problems keep
+    those rows' visible sets and scores."""
+    S, D, W = (1 << 24) + 77, 128, 64
+    scale = 1.0 / math.sqrt(D)
+    _say("long backward: generating inputs on the device")
+    q, k, v = fa_inputs.make_qkv_device(S, D, "bf16", seed=31, device="cuda")
+    dout = fa_inputs.make_qkv_device(S, D, "bf16", seed=32, device="cuda")[0]
+    torch.cuda.empty_cache()
+    o, lse = fa.flash_attn_fwd(q, k, v, causal=True, window=W, scale=scale)
+    dq, dk, dv = fa.flash_attn_bwd(q, k, v, o, lse, dout, causal=True, window=W, scale=scale)
+    torch.cuda.synchronize()
+    del o, lse
+
+    def compact(a, b):
+        idx = torch.arange(a, b, device="cuda")
+        return [fa_inputs.to_f64(t[0, 0].index_select(0, idx).cpu().reshape(1, 1, b - a, D))
+                for t in (q, k, v, dout)]
+
+    rng = np.random.default_rng(9)
+    picks = sorted(set([0, 1, 63, 64, 65, S // 2, S - 64, S - 2, S - 1, (1 << 24) - 1, 1 << 24])
+                   | set(rng.integers(0, S, size=30).tolist()))
+    err = {"dq": [0.0, 1.0], "dk": [0.0, 1.0], "dv": [0.0, 1.0]}
+    for i in picks:                       # dQ of row i
+        a = max(0, i - W + 1)
+        rq, _, _ = ORACLE.attention_bwd(*compact(a, i + 1), causal=True, scale=scale, window=W)
+        got = dq[0, 0, i].float().cpu().double().numpy()
+        err["dq"][0] = max(err["dq"][0], float(np.abs(got - rq[0, 0, i - a]).max()))
+        err["dq"][1] = max(err["dq"][1], float(np.abs(rq[0, 0, i - a]).max()))
+    for j in picks:                       # dK, dV of key j
+        a, b = max(0, j - W + 1), min(S, j + W)
+        _, rk, rv = ORACLE.attention_bwd(*compact(a, b), causal=True, scale=scale, window=W)
+        for name, t, r in (("dk", dk, rk), ("dv", dv, rv)):
+            got = t[0, 0, j].float().cpu().double().numpy()
+            err[name][0] = max(err[name][0], float(np.abs(got - r[0, 0, j - a]).max()))
+            err[name][1] = max(err[name][1], float(np.abs(r[0, 0, j - a]).max()))
+    rel = {n: e / m for n, (e, m) in err.items()}
+    _say("  long backward S=%d: " % S + " ".join(f"{n} {x:.2e}" for n, x in rel.items()))
+    assert max(rel.values()) <= TOL_G["bf16"], rel
+    del q, k, v, dout, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_backward_grouped_heads_alibi_scale(dtype):
     """Grouped K/V heads (dk, dv sum over the group), ALiBi, negative and zero
