@@ -622,10 +622,7 @@ FA_BWD_INST(_Float16, 128)
 FA_BWD_INST(_Float16, 64)
 #undef FA_BWD_INST
 
-bool bwd_supported(int D, int dtype) {
-  return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
-}
-int bwd_tile_rows() { return 32 * kBwdWaves; }
+static_assert(32 * kBwdWaves == kBwdRows && 2 * kBCf == kBwdRows, "tile sizes of the plan");
 
 template <typename T, int D, bool ALIBI>
 static hipError_t launch_bwd_a(const BwdParams& p, hipStream_t st) {

@@ -149,8 +149,14 @@ __device__ __forceinline__ void wg_coords(const FwdParams& p, int id, int& qb, i
   bh = (p.BH & 7) ? x : (x & 7) * (p.BH >> 3) + (x >> 3);
   qb = p.causal ? (p.nqb - 1 - rank) : rank;
 }
+// The work-group's position in dispatch order, or its mirror image when the
+// host asks for the reverse order (a testing aid: no work-group depends on
+// another, so the results must not change).
+__device__ __forceinline__ int wg_id(const FwdParams& p) {
+  return p.reverse ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+}
 __device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) {
-  wg_coords(p, (int)blockIdx.x, qb, bh);
+  wg_coords(p, wg_id(p), qb, bh);
 }
 
 // ALiBi bias in the base-2 logit domain: turns raw (sign-folded) scores into

@@ -314,9 +314,10 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
   // With a key split, work-group id = split * (nqb * BH) + (the id of the
   // unsplit launch); each split takes a contiguous share of the key blocks.
   const int per = p.nqb * p.BH;
-  const int split = (int)blockIdx.x / per;
+  const int id = wg_id(p);
+  const int split = id / per;
   int qb, bh;
-  wg_coords(p, (int)blockIdx.x - split * per, qb, bh);
+  wg_coords(p, id - split * per, qb, bh);
   const int S = p.S;
   const int q_lo = qb * BR;
   const size_t head = (size_t)bh * (size_t)S * D;
@@ -430,7 +431,7 @@ void fa_fwd_fast_kernel(FwdParams p) {
     // score's own bits, so such heads take the per-score |i - j| form.
     const int per = p.nqb * p.BH;
     int qb, bh;
-    wg_coords(p, (int)blockIdx.x % per, qb, bh);
+    wg_coords(p, wg_id(p) % per, qb, bh);
     if (fabsf(p.alibi[bh % p.H] * kLog2e) <= kAlibiLinMaxB2)
       fwd_body<T, D, NW, 1>(p, k0s, v0s, k1s, v1s);
     else
@@ -443,10 +444,6 @@ void fa_fwd_fast_kernel(FwdParams p) {
 // ------------------------------------------------------------------------ //
 // Host side.
 // ------------------------------------------------------------------------ //
-bool fast_supported(int D, int dtype) {
-  return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
-}
-int fast_tile_keys() { return kBCf; }
 
 // Explicit instantiations: with several instantiations of the kernel template
 // in one translation unit, the host pass emitted launch stubs only for the

@@ -502,8 +502,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
 // ------------------------------------------------------------------------ //
 // Host-side launch.
 // ------------------------------------------------------------------------ //
-int generic_tile_rows() { return kBR; }
-int generic_tile_keys() { return kBC; }
+static_assert(kBR == kGenericBR && kBC == kGenericBC, "tile sizes of the plan");
 
 template <typename K>
 static hipError_t launch_kernel(K kernel, const FwdParams& p, unsigned grid, hipStream_t st) {

@@ -10,7 +10,7 @@
 
 namespace fa {
 
-constexpr int kBCf = 64;     // keys per streamed block
+constexpr int kBCf = kFastBC;  // keys per streamed block
 constexpr float kTau = 8.f;  // lazy-rescale threshold (base-2 exponent)
 // Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format,
 // no swizzle, no stride): offsets at or past the size read as zero.

@@ -1,0 +1,86 @@
+// Host-visible description of the kernels: element types, tile sizes, the
+// parameter blocks the launches take and the kernel plan. Plain C++ with no
+// HIP dependency, so the argument validation that fills these blocks can be
+// built and tested on the host alone.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+enum { kDtypeF32 = 0, kDtypeF16 = 1, kDtypeBF16 = 2 };
+
+// Tiles. The fast bf16/f16 forward streams keys in blocks of kFastBC with 32
+// query rows per wave; the generic forward uses kGenericBR x kGenericBC tiles;
+// both backward kernels work on blocks of kBwdRows rows (queries or keys).
+constexpr int kFastBC = 64;
+constexpr int kGenericBR = 128;
+constexpr int kGenericBC = 64;
+constexpr int kBwdRows = 128;
+
+inline bool fast_supported(int64_t D, int dtype) {
+  return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
+}
+inline bool bwd_supported(int64_t D, int dtype) { return fast_supported(D, dtype); }
+
+// Arguments of one forward launch, already validated and normalised on the
+// host: window >= S is folded to 0 (no window), n_sink is clamped to S, and a
+// negative scale is folded into the sign of Q (neg = 1) so that c > 0.
+// Query head bh (= b * H + h) reads key/value head bh / G.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  unsigned long long* block_pairs;  // optional instrumentation counter (may be null)
+  const float* alibi;  // per-query-head ALiBi slopes [H], or null (no bias)
+  float* o_part;       // key-split partial outputs [n_split][BH][S][D] fp32, or null
+  float* lse_part;     // key-split partial LSE [n_split][BH][S] (with o_part)
+  int n_split;         // key-block ranges per query block (1: no split)
+  int S;        // sequence length
+  int BH;       // batch * query heads
+  int H;        // query heads
+  int G;        // query heads per key/value head
+  int nqb;      // query blocks per head = ceil(S / block_q of the chosen kernel)
+  int causal;   // 0 / 1
+  int window;   // 0 = none
+  int n_sink;   // leading always-visible keys (only with window > 0)
+  float c;      // |scale| * log2(e), at least FLT_MIN
+  int neg;      // scale < 0
+  int reverse;  // 1: work-groups take their tiles in reverse dispatch order (testing aid)
+};
+
+// Arguments of one backward launch (validated on the host). c = scale * log2(e)
+// keeps the sign of scale here: the backward kernels use the logits directly.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // forward logsumexp [BH][S]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // workspace: rowsum(dO * O) [BH][Sp], 0 past S
+  float* lse2;         // workspace: lse * log2(e) [BH][Sp], +inf past S
+  const float* alibi;  // per-query-head slopes [H], or null
+  int S, BH, H, G;     // G = query heads per key/value head
+  int Sp;              // rows per head of the workspace arrays (S rounded up to the dq block)
+  int nqb, nkb;        // query blocks of the dq kernel, key blocks of the dkv kernel
+  int causal, window, n_sink;
+  float c, scale;
+};
+
+// Which kernel and tile a problem runs with (a pure function of the shape and
+// of the FLASH_ATTN_WAVES tuning override).
+struct Plan {
+  bool fast;
+  int nw;        // waves per work-group of the fast kernel
+  int block_q;   // query rows per work-group
+  int block_k;   // keys per streamed block
+};
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype);
+
+}  // namespace fa

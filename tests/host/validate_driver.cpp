@@ -1,0 +1,374 @@
+// Host-only driver of the C ABI's argument validation (fa_validate.cpp),
+// built with AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_validate_host.py. It runs the invalid-argument table of the ABI
+// tests, checks the normalised parameters of valid calls, and then pushes
+// random extreme arguments (sizes near the int64 limits, addresses near the
+// top of the address space) through every entry so the sanitizers see any
+// overflow or out-of-bounds access. No GPU and no HIP runtime is involved.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <functional>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "../../include/flash_attn.h"
+#include "../../io_aware_tiled_flash_amd/csrc/fa_validate.h"
+
+namespace {
+
+int g_failures = 0;
+
+void expect(bool ok, const std::string& what) {
+  if (!ok) {
+    std::printf("FAIL %s\n", what.c_str());
+    ++g_failures;
+  }
+}
+
+template <typename T>
+T* addr(uintptr_t a) {
+  return reinterpret_cast<T*>(a);
+}
+
+constexpr uintptr_t Q = 0x100000, K = 0x200000, V = 0x300000, O = 0x400000, L = 0x500000;
+
+fa::FwdCall base_fwd() {
+  fa::FwdCall a;
+  a.q = addr<const void>(Q);
+  a.k = addr<const void>(K);
+  a.v = addr<const void>(V);
+  a.o = addr<void>(O);
+  a.lse = addr<float>(L);
+  a.B = 1;
+  a.H = 1;
+  a.H_kv = 1;
+  a.S = 64;
+  a.D = 64;
+  a.scale = 0.125f;
+  a.dtype = FA_BF16;
+  return a;
+}
+
+void fwd_case(const char* name, int want, const std::function<void(fa::FwdCall&)>& edit) {
+  fa::FwdCall a = base_fwd();
+  edit(a);
+  fa::FwdLaunch l;
+  std::string err;
+  const int rc = fa::prepare_fwd(a, &l, &err);
+  expect(rc == want, std::string("fwd ") + name + ": rc " + std::to_string(rc));
+  expect(rc == FA_OK || !err.empty(), std::string("fwd ") + name + ": empty message");
+}
+
+fa::BwdCall base_bwd() {
+  fa::BwdCall a;
+  a.q = addr<const void>(0x100000);
+  a.k = addr<const void>(0x200000);
+  a.v = addr<const void>(0x300000);
+  a.o = addr<const void>(0x400000);
+  a.dout = addr<const void>(0x500000);
+  a.lse = addr<const float>(0x600000);
+  a.dq = addr<void>(0x700000);
+  a.dk = addr<void>(0x800000);
+  a.dv = addr<void>(0x900000);
+  a.workspace = addr<void>(0xa00000);
+  a.workspace_bytes = 1 << 20;
+  a.B = 1;
+  a.H = 2;
+  a.H_kv = 1;
+  a.S = 64;
+  a.D = 64;
+  a.causal = 1;
+  a.scale = 0.125f;
+  a.dtype = FA_BF16;
+  return a;
+}
+
+void bwd_case(const char* name, int want, const std::function<void(fa::BwdCall&)>& edit) {
+  fa::BwdCall a = base_bwd();
+  edit(a);
+  fa::BwdParams p;
+  std::string err;
+  const int rc = fa::prepare_bwd(a, &p, &err);
+  expect(rc == want, std::string("bwd ") + name + ": rc " + std::to_string(rc));
+  expect(rc == FA_OK || !err.empty(), std::string("bwd ") + name + ": empty message");
+}
+
+// Deterministic 64-bit generator (SplitMix64) for the fuzz.
+struct Rng {
+  uint64_t s;
+  uint64_t next() {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+  // A size drawn from a mix of small values, powers of two near the int32 and
+  // int64 limits, and negatives.
+  int64_t size() {
+    const uint64_t r = next();
+    switch (r % 8) {
+      case 0: return (int64_t)(next() % 9) - 2;
+      case 1: return (int64_t)(next() % 5000);
+      case 2: return (int64_t)1 << (next() % 63);
+      case 3: return std::numeric_limits<int64_t>::max() - (int64_t)(next() % 3);
+      case 4: return std::numeric_limits<int64_t>::min() + (int64_t)(next() % 3);
+      case 5: return (int64_t)INT32_MAX - (int64_t)(next() % 300);
+      case 6: return (int64_t)(next() >> 1);
+      default: return 128;
+    }
+  }
+  uintptr_t address() {
+    const uint64_t r = next();
+    switch (r % 4) {
+      case 0: return 0;
+      case 1: return (uintptr_t)(next() & ~(uint64_t)15);
+      case 2: return ~(uintptr_t)0 - (uintptr_t)(next() % 4096);
+      default: return (uintptr_t)(0x100000 * (1 + next() % 16) + 16 * (next() % 4));
+    }
+  }
+  float scale() {
+    const uint64_t r = next() % 6;
+    if (r == 0) return std::numeric_limits<float>::infinity();
+    if (r == 1) return std::nanf("");
+    if (r == 2) return 0.f;
+    if (r == 3) return -0.0883883f;
+    if (r == 4) return std::numeric_limits<float>::max();
+    return 0.0883883f;
+  }
+};
+
+}  // namespace
+
+int main() {
+  // ---- forward: each precondition of flash_attn.h ----
+  fwd_case("valid", FA_OK, [](fa::FwdCall&) {});
+  fwd_case("null_q", FA_ERR_INVALID, [](fa::FwdCall& a) { a.q = nullptr; });
+  fwd_case("null_k", FA_ERR_INVALID, [](fa::FwdCall& a) { a.k = nullptr; });
+  fwd_case("null_v", FA_ERR_INVALID, [](fa::FwdCall& a) { a.v = nullptr; });
+  fwd_case("null_o", FA_ERR_INVALID, [](fa::FwdCall& a) { a.o = nullptr; });
+  fwd_case("null_lse", FA_ERR_INVALID, [](fa::FwdCall& a) { a.lse = nullptr; });
+  fwd_case("B0", FA_ERR_INVALID, [](fa::FwdCall& a) { a.B = 0; });
+  fwd_case("H0", FA_ERR_INVALID, [](fa::FwdCall& a) { a.H = 0; });
+  fwd_case("S0", FA_ERR_INVALID, [](fa::FwdCall& a) { a.S = 0; });
+  fwd_case("S_negative", FA_ERR_INVALID, [](fa::FwdCall& a) { a.S = -5; });
+  fwd_case("D0", FA_ERR_INVALID, [](fa::FwdCall& a) { a.D = 0; });
+  fwd_case("causal_2", FA_ERR_INVALID, [](fa::FwdCall& a) { a.causal = 2; });
+  fwd_case("window_negative", FA_ERR_INVALID, [](fa::FwdCall& a) { a.causal = 1; a.window = -1; });
+  fwd_case("window_without_causal", FA_ERR_INVALID, [](fa::FwdCall& a) { a.window = 16; });
+  fwd_case("n_sink_negative", FA_ERR_INVALID,
+           [](fa::FwdCall& a) { a.causal = 1; a.window = 16; a.n_sink = -1; });
+  fwd_case("scale_nan", FA_ERR_INVALID, [](fa::FwdCall& a) { a.scale = std::nanf(""); });
+  fwd_case("scale_inf", FA_ERR_INVALID,
+           [](fa::FwdCall& a) { a.scale = std::numeric_limits<float>::infinity(); });
+  fwd_case("dtype_unknown", FA_ERR_INVALID, [](fa::FwdCall& a) { a.dtype = 3; });
+  fwd_case("q_misaligned", FA_ERR_INVALID, [](fa::FwdCall& a) { a.q = addr<const void>(Q + 8); });
+  fwd_case("lse_misaligned", FA_ERR_INVALID, [](fa::FwdCall& a) { a.lse = addr<float>(L + 2); });
+  fwd_case("o_overlaps_q", FA_ERR_INVALID, [](fa::FwdCall& a) { a.o = addr<void>(Q + 64); });
+  fwd_case("lse_overlaps_o", FA_ERR_INVALID, [](fa::FwdCall& a) { a.lse = addr<float>(O + 128); });
+  fwd_case("size_overflow", FA_ERR_INVALID,
+           [](fa::FwdCall& a) { a.B = (int64_t)1 << 40; a.H = (int64_t)1 << 20; a.S = 1024; });
+  fwd_case("kv_heads_not_dividing", FA_ERR_INVALID, [](fa::FwdCall& a) { a.H = 6; a.H_kv = 4; });
+  fwd_case("alibi_overlaps_lse", FA_ERR_INVALID,
+           [](fa::FwdCall& a) { a.alibi = addr<const float>(L); });
+  fwd_case("counter_misaligned", FA_ERR_INVALID,
+           [](fa::FwdCall& a) { a.block_pairs = addr<uint64_t>(0x600004); });
+  fwd_case("split_no_workspace", FA_ERR_INVALID, [](fa::FwdCall& a) { a.n_split = 2; });
+  fwd_case("split_too_many", FA_ERR_INVALID, [](fa::FwdCall& a) { a.n_split = 257; });
+  fwd_case("split_small_workspace", FA_ERR_INVALID, [](fa::FwdCall& a) {
+    a.n_split = 2;
+    a.workspace = addr<void>(0x800000);
+    a.workspace_bytes = 16;
+  });
+  fwd_case("split_f32", FA_ERR_UNSUPPORTED, [](fa::FwdCall& a) {
+    a.n_split = 2;
+    a.dtype = FA_F32;
+    a.workspace = addr<void>(0x800000);
+    a.workspace_bytes = 1 << 20;
+  });
+  fwd_case("head_dim_96", FA_ERR_UNSUPPORTED, [](fa::FwdCall& a) { a.D = 96; });
+  fwd_case("index_range", FA_ERR_UNSUPPORTED, [](fa::FwdCall& a) {
+    a.S = (int64_t)1 << 31;
+    a.D = 16;
+    a.o = addr<void>((uintptr_t)1 << 44);
+    a.lse = addr<float>((uintptr_t)1 << 45);
+  });
+  fwd_case("grid_range", FA_ERR_UNSUPPORTED, [](fa::FwdCall& a) {
+    a.B = (int64_t)1 << 20;
+    a.S = 1 << 20;
+    a.D = 16;
+    a.k = addr<const void>((uintptr_t)1 << 46);
+    a.v = addr<const void>((uintptr_t)1 << 47);
+    a.o = addr<void>((uintptr_t)1 << 48);
+    a.lse = addr<float>((uintptr_t)1 << 49);
+  });
+
+  // ---- forward: normalisation of a valid call ----
+  {
+    fa::FwdCall a = base_fwd();
+    a.B = 2;
+    a.H = 8;
+    a.H_kv = 2;
+    a.S = 1000;
+    a.D = 128;
+    a.causal = 1;
+    a.window = 5000;   // wider than S: no window
+    a.n_sink = 9;
+    a.scale = -0.25f;
+    a.q = addr<const void>(0x10000000);
+    a.k = addr<const void>(0x20000000);
+    a.v = addr<const void>(0x30000000);
+    a.o = addr<void>(0x40000000);
+    a.lse = addr<float>(0x50000000);
+    fa::FwdLaunch l;
+    std::string err;
+    expect(fa::prepare_fwd(a, &l, &err) == FA_OK, "normalise: rc");
+    expect(l.p.window == 0 && l.p.n_sink == 0, "normalise: window folded");
+    expect(l.p.neg == 1 && std::fabs(l.p.c - 0.25f * 1.4426950408889634f) < 1e-6f, "normalise: scale");
+    expect(l.p.G == 4 && l.p.BH == 16 && l.p.S == 1000, "normalise: heads");
+    expect(l.plan.fast && l.p.nqb == (1000 + l.plan.block_q - 1) / l.plan.block_q, "normalise: plan");
+    expect(l.rows == 16000, "normalise: rows");
+    a.window = 100;
+    a.n_sink = 5000;
+    expect(fa::prepare_fwd(a, &l, &err) == FA_OK && l.p.window == 100 && l.p.n_sink == 1000,
+           "normalise: sinks clamped to S");
+    a.scale = 0.f;
+    expect(fa::prepare_fwd(a, &l, &err) == FA_OK && l.p.c > 0.f && l.p.neg == 0,
+           "normalise: zero scale");
+  }
+
+  // ---- backward ----
+  bwd_case("valid", FA_OK, [](fa::BwdCall&) {});
+  bwd_case("null_dq", FA_ERR_INVALID, [](fa::BwdCall& a) { a.dq = nullptr; });
+  bwd_case("null_workspace", FA_ERR_INVALID, [](fa::BwdCall& a) { a.workspace = nullptr; });
+  bwd_case("small_workspace", FA_ERR_INVALID, [](fa::BwdCall& a) { a.workspace_bytes = 8; });
+  bwd_case("dk_overlaps_k", FA_ERR_INVALID,
+           [](fa::BwdCall& a) { a.dk = addr<void>(0x200000 + 16); });
+  bwd_case("dq_overlaps_dv", FA_ERR_INVALID, [](fa::BwdCall& a) { a.dq = addr<void>(0x900000); });
+  bwd_case("misaligned_dout", FA_ERR_INVALID,
+           [](fa::BwdCall& a) { a.dout = addr<const void>(0x500008); });
+  bwd_case("f32", FA_ERR_UNSUPPORTED, [](fa::BwdCall& a) { a.dtype = FA_F32; });
+  bwd_case("d32", FA_ERR_UNSUPPORTED, [](fa::BwdCall& a) { a.D = 32; });
+  bwd_case("window_no_causal", FA_ERR_INVALID, [](fa::BwdCall& a) { a.causal = 0; a.window = 4; });
+
+  // ---- merge and sizes ----
+  {
+    std::string err;
+    const float* op = addr<const float>(0x100000);
+    const float* lp = addr<const float>(0x200000);
+    expect(fa::check_merge(op, lp, 4, 64, 64, addr<void>(0x300000), addr<float>(0x400000), FA_BF16,
+                           &err) == FA_OK, "merge valid");
+    expect(fa::check_merge(op, lp, 4, 64, 64, addr<void>(0x100010), addr<float>(0x400000), FA_BF16,
+                           &err) == FA_ERR_INVALID, "merge overlap");
+    expect(fa::check_merge(op, lp, 0, 64, 64, addr<void>(0x300000), addr<float>(0x400000), FA_BF16,
+                           &err) == FA_ERR_INVALID, "merge n_parts");
+    expect(fa::split_workspace_bytes(1, 8, 4096, 128, 1, &err) == 0, "split ws n=1");
+    expect(fa::split_workspace_bytes(1, 8, 4096, 128, 4, &err) ==
+               (int64_t)4 * 8 * 4096 * 128 * 4 + 4 * 8 * 4096 * 4, "split ws size");
+    expect(fa::bwd_workspace_bytes(4, 16, 4096, &err) == 2 * 64 * 4096 * 4, "bwd ws size");
+    expect(fa::bwd_workspace_bytes(1, 1, 0, &err) == -1, "bwd ws invalid");
+    int bq = 0, bk = 0;
+    expect(fa::tile_shape(1, 1, 64, 48, FA_BF16, &bq, &bk, &err) == FA_ERR_UNSUPPORTED, "tile d48");
+    expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, &bq, &bk, &err) == FA_OK && bk == fa::kFastBC,
+           "tile c3");
+  }
+
+  // ---- fuzz: random extreme arguments through every entry ----
+  Rng rng{12345};
+  int ok_fwd = 0, ok_bwd = 0;
+  for (int it = 0; it < 200000; ++it) {
+    fa::FwdCall a;
+    a.q = addr<const void>(rng.address());
+    a.k = addr<const void>(rng.address());
+    a.v = addr<const void>(rng.address());
+    a.o = addr<void>(rng.address());
+    a.lse = addr<float>(rng.address());
+    a.B = rng.size();
+    a.H = rng.size();
+    a.H_kv = (rng.next() & 1) ? a.H : rng.size();
+    a.S = rng.size();
+    a.D = (rng.next() & 1) ? (int64_t)16 << (rng.next() % 4) : rng.size();
+    a.causal = (int)(rng.next() % 3);
+    a.window = rng.size();
+    a.n_sink = rng.size();
+    a.scale = rng.scale();
+    a.alibi = (rng.next() & 1) ? nullptr : addr<const float>(rng.address());
+    a.dtype = (int)(rng.next() % 4);
+    a.block_pairs = (rng.next() & 3) ? nullptr : addr<uint64_t>(rng.address());
+    a.n_split = (rng.next() & 1) ? 1 : rng.size();
+    a.workspace = addr<void>(rng.address());
+    a.workspace_bytes = rng.size();
+    if (it & 1) {
+      // mostly valid: disjoint, aligned tensors 2^40 bytes apart and sizes
+      // that fit, with the random mask, scale, dtype and split kept
+      a.q = addr<const void>((uintptr_t)1 << 40);
+      a.k = addr<const void>((uintptr_t)2 << 40);
+      a.v = addr<const void>((uintptr_t)3 << 40);
+      a.o = addr<void>((uintptr_t)4 << 40);
+      a.lse = addr<float>((uintptr_t)5 << 40);
+      a.alibi = (rng.next() & 1) ? nullptr : addr<const float>((uintptr_t)6 << 40);
+      a.block_pairs = nullptr;
+      a.workspace = addr<void>((uintptr_t)7 << 40);
+      a.workspace_bytes = (int64_t)1 << 40;
+      a.B = 1 + (int64_t)(rng.next() % 8);
+      a.H_kv = 1 + (int64_t)(rng.next() % 4);
+      a.H = a.H_kv * (1 + (int64_t)(rng.next() % 4));
+      a.S = 1 + (int64_t)(rng.next() % 70000);
+      a.D = (int64_t)16 << (rng.next() % 4);
+      a.n_split = 1 + (int64_t)(rng.next() % 8);
+      a.window = (int64_t)(rng.next() % 3) * (int64_t)(rng.next() % 100000);
+      a.n_sink = (int64_t)(rng.next() % 9);
+      if (a.window > 0) a.causal = 1;
+    }
+    fa::FwdLaunch l;
+    std::string err;
+    if (fa::prepare_fwd(a, &l, &err) == FA_OK) {
+      ++ok_fwd;
+      expect(l.p.S >= 1 && l.p.BH >= 1 && l.p.nqb >= 1 && l.p.c > 0.f, "fuzz fwd accepted sanely");
+      expect(l.p.window >= 0 && l.p.window < l.p.S + (l.p.window == 0) && l.p.n_sink <= l.p.S &&
+                 (l.p.window > 0 || l.p.n_sink == 0) && (int64_t)l.p.nqb * l.plan.block_q >= l.p.S,
+             "fuzz fwd normalised mask and grid");
+    }
+    fa::BwdCall b;
+    b.q = addr<const void>(rng.address());
+    b.k = addr<const void>(rng.address());
+    b.v = addr<const void>(rng.address());
+    b.o = addr<const void>(rng.address());
+    b.dout = addr<const void>(rng.address());
+    b.lse = addr<const float>(rng.address());
+    b.dq = addr<void>(rng.address());
+    b.dk = addr<void>(rng.address());
+    b.dv = addr<void>(rng.address());
+    b.workspace = addr<void>(rng.address());
+    b.workspace_bytes = rng.size();
+    b.B = rng.size();
+    b.H = rng.size();
+    b.H_kv = (rng.next() & 1) ? b.H : rng.size();
+    b.S = rng.size();
+    b.D = (rng.next() & 1) ? 64 : rng.size();
+    b.causal = (int)(rng.next() % 3);
+    b.window = rng.size();
+    b.n_sink = rng.size();
+    b.scale = rng.scale();
+    b.dtype = (int)(rng.next() % 4);
+    fa::BwdParams bp;
+    if (fa::prepare_bwd(b, &bp, &err) == FA_OK) ++ok_bwd;
+    (void)fa::check_merge(addr<const float>(rng.address()), addr<const float>(rng.address()),
+                          rng.size(), rng.size(), rng.size(), addr<void>(rng.address()),
+                          addr<float>(rng.address()), (int)(rng.next() % 4), &err);
+    (void)fa::split_workspace_bytes(rng.size(), rng.size(), rng.size(), rng.size(), rng.size(),
+                                    &err);
+    (void)fa::bwd_workspace_bytes(rng.size(), rng.size(), rng.size(), &err);
+    int bq, bk;
+    (void)fa::tile_shape(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4), &bq,
+                         &bk, &err);
+  }
+  std::printf("fuzz: %d forward and %d backward calls accepted of 200000 each\n", ok_fwd, ok_bwd);
+  if (g_failures) {
+    std::printf("%d FAILURES\n", g_failures);
+    return 1;
+  }
+  std::printf("ALL OK\n");
+  return 0;
+}
