@@ -107,6 +107,29 @@ def _check(rc: int):
     raise RuntimeError(f"flash_attn error {rc}: {msg}")
 
 
+def _check_device_tensor(name, t, device, dtype=None, shape=None):
+    """t must be a contiguous torch tensor on `device` (and of dtype / shape
+    when given): the library receives only its address, so nothing below
+    this line could catch a host tensor or a short buffer."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+
+
+def _check_workspace(t, device, need: int):
+    _check_device_tensor("workspace", t, device)
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+
+
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -157,6 +180,8 @@ def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alib
                 _check(FA_ERR_INVALID)
             if workspace is None and need > 0:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif workspace is not None:
+                _check_workspace(workspace, q.device, need)
             ws_ptr = None if workspace is None else workspace.data_ptr()
             ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
             slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
@@ -227,14 +252,16 @@ def flash_attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None):
         raise ValueError("partials must be contiguous GPU tensors")
     if o_parts.dim() < 2 or o_parts.shape[:-1] != lse_parts.shape:
         raise ValueError("o_parts must be [n, ..., D] and lse_parts [n, ...]")
+    if lse_parts.device != o_parts.device:
+        raise ValueError("o_parts and lse_parts must be on one device")
     n, D = o_parts.shape[0], o_parts.shape[-1]
     rows = lse_parts[0].numel()
+    dev = o_parts.device
     dtype = torch.float32 if dtype is None else dtype
-    o = torch.empty(o_parts.shape[1:], dtype=dtype, device=o_parts.device) if out is None else out
-    l = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device) \
-        if lse is None else lse
-    if o.shape != o_parts.shape[1:] or not o.is_contiguous() or l.shape != lse_parts.shape[1:]:
-        raise ValueError("out / lse shapes do not match the partials")
+    o = torch.empty(o_parts.shape[1:], dtype=dtype, device=dev) if out is None else out
+    l = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=dev) if lse is None else lse
+    _check_device_tensor("out", o, dev, dtype=dtype, shape=o_parts.shape[1:])
+    _check_device_tensor("lse", l, dev, dtype=torch.float32, shape=lse_parts.shape[1:])
     with torch.cuda.device(o_parts.device):
         stream = torch.cuda.current_stream(o_parts.device).cuda_stream
         rc = capi().flash_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, rows, D,
@@ -250,13 +277,8 @@ def flash_attn_bwd_workspace_bytes(B: int, H: int, S: int) -> int:
     return n
 
 
-def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int = 0,
-                   n_sink: int = 0, scale: float | None = None, alibi_slopes=None,
-                   workspace=None, dq=None, dk=None, dv=None):
-    """Gradients (dq, dk, dv) of flash_attn_fwd on the GPU, recomputed from the
-    forward's o and lse. q, o, dout: [B, H, S, D]; k, v: [B, H_kv, S, D]; lse:
-    fp32 [B, H, S]; bf16 / f16 with D 64 or 128. workspace: optional GPU tensor
-    of at least flash_attn_bwd_workspace_bytes(B, H, S) bytes."""
+def _bwd_args(q, k, v, o, lse, dout, scale, alibi_slopes, dq, dk, dv):
+    """Checks of the backward's tensors; returns (B, H, Hkv, S, D, scale, dq, dk, dv)."""
     import torch
     ts = {"q": q, "k": k, "v": v, "o": o, "dout": dout}
     for name, t in ts.items():
@@ -270,24 +292,35 @@ def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int =
     if o.shape != q.shape or dout.shape != q.shape or k.shape != (B, Hkv, S, D) \
             or v.shape != k.shape:
         raise ValueError("q, o, dout: [B, H, S, D]; k, v: [B, H_kv, S, D]")
-    if not isinstance(lse, torch.Tensor) or lse.shape != (B, H, S) or \
-            lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, S] on q's device")
-    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
-                                     alibi_slopes.shape != (H,) or not alibi_slopes.is_cuda):
-        raise ValueError("alibi_slopes must be a float32 GPU tensor [H]")
+    _check_device_tensor("lse", lse, q.device, dtype=torch.float32, shape=(B, H, S))
+    if alibi_slopes is not None:
+        _check_device_tensor("alibi_slopes", alibi_slopes, q.device, dtype=torch.float32,
+                             shape=(H,))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
-                or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor like its input")
+        _check_device_tensor(name, t, q.device, dtype=ref.dtype, shape=ref.shape)
+    return B, H, Hkv, S, D, scale, dq, dk, dv
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int = 0,
+                   n_sink: int = 0, scale: float | None = None, alibi_slopes=None,
+                   workspace=None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of flash_attn_fwd on the GPU, recomputed from the
+    forward's o and lse. q, o, dout: [B, H, S, D]; k, v: [B, H_kv, S, D]; lse:
+    fp32 [B, H, S]; bf16 / f16 with D 64 or 128. workspace: optional GPU tensor
+    of at least flash_attn_bwd_workspace_bytes(B, H, S) bytes."""
+    import torch
+    B, H, Hkv, S, D, scale, dq, dk, dv = _bwd_args(q, k, v, o, lse, dout, scale, alibi_slopes,
+                                                   dq, dk, dv)
     need = flash_attn_bwd_workspace_bytes(B, H, S)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, q.device, need)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = capi().flash_attn_bwd(

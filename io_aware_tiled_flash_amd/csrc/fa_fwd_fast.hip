@@ -71,9 +71,9 @@ struct Core {
   int koff[NS];      // LDS offsets of the K fragment per k-step
   int vdt[NDT];      // LDS offsets of the V^T fragment reads per d tile
   f32x16 oacc[NDT];  // O^T accumulator
-  float m_run;       // running max (raw sign-folded score units)
+  float m_run;       // reference max (raw sign-folded score units)
   float mc;          // m_run * c, or 0 while nothing is visible
-  float l[4];        // this lane half's running sum, in 4 parts
+  float l_run;       // this lane half's running sum of the weights
   float c, tau_raw;  // softmax scale (1 for AL == 2, whose logits come scaled)
   float b2;          // ALiBi slope in base 2 (AL != 0)
   float beta;        // b2 / c: the ALiBi slope in raw score units (AL == 1)
@@ -107,8 +107,7 @@ struct Core {
       for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
     m_run = kNegInf;
     mc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) l[k] = 0.f;
+    l_run = 0.f;
     c = (AL == 2) ? 1.f : p.c;
     beta = (AL == 1) ? b2 / p.c : 0.f;
     tau_raw = kTau / c;
@@ -172,17 +171,17 @@ struct Core {
     }
   }
 
-  // Online softmax with lazy rescale: turns the (masked) scores into p,
-  // adds them to l and packs them into the B operands of the PV MFMA.
-  // off (AL == 1 only): this lane's ALiBi offset for the block, added to
-  // every score the lane holds after the per-key ramp (see alibi_ramp).
-  __device__ __forceinline__ void softmax(f32x16 (&acc)[NT], v8 (&pb)[NT][2], float off = 0.f) {
-    // Row max: one chain of three-input maxima per 32-key sub-tile, the
-    // first seeded with the running max (the lane pair holding a row shares
-    // it), then the exchange across the half-waves.
-    // Sub-tile 0: the running max and 16 scores (8 v_maximum3); later
+  // Reference max update with lazy rescale. The block's row max (two chains
+  // of three-input maxima, one per 32-key sub-tile, the first seeded with
+  // the reference, then the exchange across the half-waves) moves the
+  // reference only when it exceeds it by more than tau (2^8 in base 2); O and
+  // l are then rescaled. The decision is wave-uniform, so the rescale is
+  // skipped as a branch. off (AL == 1 only): this lane's ALiBi offset for the
+  // block (see alibi_ramp).
+  __device__ __forceinline__ void max_update(const f32x16 (&acc)[NT], float off) {
+    // Sub-tile 0: the reference and 16 scores (8 v_maximum3); later
     // sub-tiles: 15 scores (7), their 16th joins the final maximum3. With
-    // the ALiBi offset the running max joins after the offset is added.
+    // the ALiBi offset the reference joins after the offset is added.
     float mj = (AL == 1) ? vmax(acc[0][0], acc[0][1]) : vmax(vmax(m_run, acc[0][0]), acc[0][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mj = vmax(vmax(mj, acc[0][r]), acc[0][r + 1]);
@@ -200,56 +199,87 @@ struct Core {
       const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(mc - mc_new);
       m_run = m_new;
       mc = mc_new;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) l[k] *= alpha;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
-    const float bo = (AL == 1) ? __builtin_fmaf(off, c, -mc) : -mc;
+  }
+
+  // Exponent bias of the block: p = exp2(c s + bias).
+  __device__ __forceinline__ float bias(float off) const {
+    return (AL == 1) ? __builtin_fmaf(off, c, -mc) : -mc;
+  }
+
+  // Chunk TU = 2t + u of a block holds the 16 keys 32t + 16u .. +15; this
+  // lane's 8 of them are acc[t][8u .. 8u + 7]. exp_chunk turns them into
+  // p = exp2(c s + bias), adds them to the four partial sums ls (fp32, so the
+  // logsumexp sees the weights unrounded) and packs p to T (nearest even) as
+  // the B operand of the PV MFMA.
+  template <int TU>
+  __device__ __forceinline__ void exp_chunk(f32x16 (&acc)[NT], v8& pbc, float bo,
+                                            float (&ls)[4]) const {
+    constexpr int t = TU >> 1, u = TU & 1;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int r = 0; r < 8; ++r) {
+      const float e = fast_exp2(__builtin_fmaf(acc[t][8 * u + r], c, bo));
+      acc[t][8 * u + r] = e;
+      ls[r & 3] += e;
+    }
+    u32x4 w;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(acc[t][r], c, bo));
-        acc[t][r] = e;
-        l[r & 3] += e;
-      }
+    for (int j = 0; j < 4; ++j) w[j] = pack2<T>(acc[t][8 * u + 2 * j], acc[t][8 * u + 2 * j + 1]);
+    pbc = __builtin_bit_cast(v8, w);
+  }
+
+  // The weights of the whole block; returns l_run plus their sum (four add
+  // chains, one of them starting from l_run).
+  __device__ __forceinline__ float exp_block(f32x16 (&acc)[NT], v8 (&pb)[4], float bo) const {
+    float ls[4] = {l_run, 0.f, 0.f, 0.f};
+    exp_chunk<0>(acc, pb[0], bo, ls);
+    exp_chunk<1>(acc, pb[1], bo, ls);
+    exp_chunk<2>(acc, pb[2], bo, ls);
+    exp_chunk<3>(acc, pb[3], bo, ls);
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  }
+
+  // O^T += V^T P^T for the V tile at vs, chunk by chunk.
+  __device__ __forceinline__ void pv(const T* vs, const v8 (&pb)[4]) {
+    u32x4 vf[NDT];
+    v_read<0>(vs, vf);
+    pv_chunk(vf, pb[0]);
+    v_read<1>(vs, vf);
+    pv_chunk(vf, pb[1]);
+    v_read<2>(vs, vf);
+    pv_chunk(vf, pb[2]);
+    v_read<3>(vs, vf);
+    pv_chunk(vf, pb[3]);
+  }
+
+  // V^T fragments of chunk TU for every d tile: two transposing reads each.
+  template <int TU>
+  __device__ __forceinline__ void v_read(const T* vs, u32x4 (&vf)[NDT]) const {
+    const T* vk = vs + (16 * TU) * D;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 w;
-        w[0] = pack2<T>(acc[t][8 * u + 0], acc[t][8 * u + 1]);
-        w[1] = pack2<T>(acc[t][8 * u + 2], acc[t][8 * u + 3]);
-        w[2] = pack2<T>(acc[t][8 * u + 4], acc[t][8 * u + 5]);
-        w[3] = pack2<T>(acc[t][8 * u + 6], acc[t][8 * u + 7]);
-        pb[t][u] = __builtin_bit_cast(v8, w);
-      }
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x2 lo = lds_tr_read(vk + vdt[dt]);
+      const u32x2 hi = lds_tr_read(vk + 8 * D + vdt[dt]);
+      vf[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
 
-  // O^T += V^T P^T for the V tile at vs (two transposed reads per operand).
-  __device__ __forceinline__ void pv(const T* vs, const v8 (&pb)[NT][2]) {
+  // O^T += V^T P^T over one chunk's 16 keys.
+  __device__ __forceinline__ void pv_chunk(const u32x4 (&vf)[NDT], v8 pbc) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const T* vk = vs + (32 * t + 16 * u) * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x2 lo = lds_tr_read(vk + vdt[dt]);
-          const u32x2 hi = lds_tr_read(vk + 8 * D + vdt[dt]);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[dt] = Tr::mma(__builtin_bit_cast(v8, w), pb[t][u], oacc[dt]);
-        }
-      }
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = Tr::mma(__builtin_bit_cast(v8, vf[dt]), pbc, oacc[dt]);
   }
 
   // Partial result of a key split: O_r = O / l in fp32 and LSE_r into the
   // workspace ([split][B*H][S][D] and [split][B*H][S]); a row that saw no key
   // of this split gets (0, -inf).
   __device__ __forceinline__ void epilogue_partial(const FwdParams& p, int split, int bh) {
-    const float l_tot = xhalf_sum((l[0] + l[1]) + (l[2] + l[3]));
+    const float l_tot = xhalf_sum(l_run);
     if (i < p.S) {
       const size_t row = ((size_t)split * p.BH + bh) * (size_t)p.S + i;
       const bool any = l_tot > 0.f;
@@ -270,7 +300,7 @@ struct Core {
 
   // O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.
   __device__ __forceinline__ void epilogue(const FwdParams& p, size_t head, int bh) {
-    const float l_tot = xhalf_sum((l[0] + l[1]) + (l[2] + l[3]));
+    const float l_tot = xhalf_sum(l_run);
     if (i < p.S) {
       const float inv = 1.f / l_tot;
       T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head + (size_t)i * D;
@@ -362,9 +392,18 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
   // [partially visible blocks][fully visible blocks][partially visible
   // blocks] (sinks and the window's first blocks, the interior, the causal
   // diagonal), and each segment runs its own copy of the loop, so the common
-  // fully visible step carries no mask code and no branch around it.
+  // fully visible step carries no mask code and no branch around it. Every
+  // block takes the row max and the lazy rescale before its weights, and the
+  // weights and the PV products then form one stretch of code, which lets the
+  // compiler interleave a wave's exponentials with its own PV MFMAs. (Dropping
+  // the row max in fully visible blocks, with a check of the block's sum of
+  // weights before the PV products, saves ~30 VALU instructions per block but
+  // puts a branch between the two; measured on the causal B4 H16 S4096 D128
+  // workload, that ran 4 % slower.)
+  static_assert(C::NT == 2, "four 16-key chunks per block");
   auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
+    constexpr bool MASK = decltype(mask)::value;
     T* kc = PAR == 0 ? k0s : k1s;
     T* vc = PAR == 0 ? v0s : v1s;
     T* kn = PAR == 0 ? k1s : k0s;
@@ -377,16 +416,17 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
     // In a partially visible block, a wave whose 32 rows see none of its keys
     // (above the causal diagonal, or before the window) skips the block.
     const int k0 = kb(it) * BC;
-    if (!decltype(mask)::value ||
-        !block_hidden<BC>(q_lo + 32 * wave, q_lo + 32 * wave + 31, k0, p.causal, p.window,
-                          p.n_sink)) {
+    if (!MASK || !block_hidden<BC>(q_lo + 32 * wave, q_lo + 32 * wave + 31, k0, p.causal,
+                                   p.window, p.n_sink)) {
       f32x16 sacc[C::NT];
       core.qk(sacc, kc);
-      if (decltype(mask)::value) core.mask(sacc, p, k0);
+      if (MASK) core.mask(sacc, p, k0);
       if (AL == 2) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
       if (AL == 1) alibi_ramp<C::NT>(sacc, core.beta);
-      typename C::v8 pb[C::NT][2];
-      core.softmax(sacc, pb, AL == 1 ? core.beta * (float)(k0 + 4 * core.h - core.i) : 0.f);
+      const float off = AL == 1 ? core.beta * (float)(k0 + 4 * core.h - core.i) : 0.f;
+      core.max_update(sacc, off);
+      typename C::v8 pb[4];
+      core.l_run = core.exp_block(sacc, pb, core.bias(off));
       core.pv(vc, pb);
     }
     wait_vmem<0>();
@@ -461,6 +501,8 @@ FA_FAST_INST(_Float16, 128, 4)
 FA_FAST_INST(_Float16, 64, 8)
 FA_FAST_INST(_Float16, 64, 4)
 #undef FA_FAST_INST
+
+
 
 template <typename T, int D, int AL>
 static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {

@@ -333,9 +333,9 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   p.dk = a.dk;
   p.dv = a.dv;
   const int64_t sp = nb * br;   // rows per head of the two workspace arrays
-  p.delta = static_cast<float*>(a.workspace);
-  p.lse2 = static_cast<float*>(a.workspace) + B * H * sp;
   p.Sp = (int)sp;
+  p.BH = (int)(B * H);
+  bwd_bind_workspace(&p, a.workspace);
   p.alibi = a.alibi;
   p.S = (int)S;
   p.BH = (int)(B * H);
@@ -349,6 +349,11 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   p.scale = a.scale;
   p.c = (float)((double)a.scale * 1.4426950408889634);
   return FA_OK;
+}
+
+void bwd_bind_workspace(BwdParams* p, void* ws) {
+  p->delta = static_cast<float*>(ws);
+  p->lse2 = ws ? static_cast<float*>(ws) + (int64_t)p->BH * p->Sp : nullptr;
 }
 
 int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q, int* block_k,

@@ -67,6 +67,9 @@ struct BwdCall {
 
 int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err);
 
+// Points the backward's two per-row arrays into the workspace ws.
+void bwd_bind_workspace(BwdParams* p, void* ws);
+
 // flash_attn_merge's checks.
 int check_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, int64_t rows,
                 int64_t D, const void* o, const float* lse, int dtype, std::string* err);

@@ -305,3 +305,4 @@ def test_bwd_workspace_bytes():
     assert fa.capi().flash_attn_bwd_workspace_bytes(2, 3, 100) == 2 * 2 * 3 * 128 * 4
     assert fa.capi().flash_attn_bwd_workspace_bytes(1, 1, 129) == (2 * 256 * 4 + 255) // 256 * 256
     assert fa.capi().flash_attn_bwd_workspace_bytes(0, 3, 100) == -1
+

@@ -315,6 +315,61 @@ def test_sharp_softmax_and_key_offset(dtype):
             label=f"{dtype} key offset")
 
 
+def _spiked_inputs(B, H, S, D, dtype, seed, pattern):
+    """Q, K, V whose scores jump far above everything before them at chosen
+    keys: Q gains a common direction u (|u| = 1, q.u about 4), and key j gains
+    g_j u, which lifts its score against every query by about 4 g_j / sqrt(D)
+    (natural-log units at scale 1/sqrt(D)). "spikes": keys 300, 700 and 1000
+    jump by 20, 40 and 60; "ramp": every key j rises by 20 per 64-key block
+    over the previous block."""
+    q, k, v = fa_inputs.make_qkv(B, H, S, D, "f32", seed=seed)
+    u = torch.from_numpy(np.random.default_rng(seed + 100).standard_normal(D).astype(np.float32))
+    u = u / u.norm()
+    q = q + 4.0 * u
+    g = torch.zeros(S)
+    if pattern == "spikes":
+        for j, lift in ((300, 20.0), (700, 40.0), (1000, 60.0)):
+            if j < S:
+                g[j] = lift * math.sqrt(D) / 4.0
+    else:
+        g = torch.div(torch.arange(S), 64, rounding_mode="floor").float() * 20.0 * math.sqrt(D) / 4.0
+    k = k + g[None, None, :, None] * u
+    tdt = fa_inputs.DTYPES[dtype]
+    return q.to(tdt), k.to(tdt), v.to(tdt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pattern", ["spikes", "ramp"])
+def test_score_jumps_in_visible_blocks(dtype, D, pattern):
+    """Scores that jump far above the running max inside fully visible blocks,
+    deep in the sequence: the kernel's lazy rescale keeps a stale reference
+    max until a block's max exceeds it by more than 2^8 (base 2), so each
+    jump must move the reference and rescale O and l at once (a weight formed
+    against the old reference would overflow fp32, or f16). Single jumps of
+    20, 40 and 60 (natural-log units) and a ramp that rises by 20 every block;
+    causal, with a window and sinks, with a key split, with ALiBi, and
+    without a mask."""
+    S = 1100 if pattern == "spikes" else 700
+    q, k, v = _spiked_inputs(1, 2, S, D, dtype, seed=21, pattern=pattern)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = gpu_fwd(q, k, v, causal=True, scale=scale)
+    compare(o, lse, q, k, v, dtype, causal=True, scale=scale, label=f"{dtype} D{D} {pattern}")
+    o, lse = gpu_fwd(q, k, v, causal=True, window=500, n_sink=3, scale=scale)
+    compare(o, lse, q, k, v, dtype, causal=True, window=500, n_sink=3, scale=scale,
+            label=f"{dtype} D{D} {pattern} window")
+    o, lse = fa.flash_attn_fwd_split(q.cuda(), k.cuda(), v.cuda(), n_split=3, causal=True,
+                                     scale=scale)
+    torch.cuda.synchronize()
+    compare(o, lse, q, k, v, dtype, causal=True, scale=scale, label=f"{dtype} D{D} {pattern} split")
+    slopes = np.array([0.01, 0.002], dtype=np.float32)
+    o, lse = gpu_fwd(q, k, v, causal=True, scale=scale, alibi_slopes=torch.from_numpy(slopes).cuda())
+    compare(o, lse, q, k, v, dtype, causal=True, scale=scale, alibi=slopes.astype(np.float64),
+            label=f"{dtype} D{D} {pattern} alibi")
+    o, lse = gpu_fwd(q, k, v, causal=False, scale=scale)
+    compare(o, lse, q, k, v, dtype, causal=False, scale=scale, label=f"{dtype} D{D} {pattern} full")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_scale_zero_and_negative(dtype):
     """scale = 0: every visible key weighs the same (O = mean of visible V,
@@ -366,6 +421,45 @@ def test_deterministic_bitwise():
     for _ in range(10):
         o, l = fa.flash_attn_fwd(qd, kd, vd, causal=True, window=300, n_sink=4)
         assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
+def test_grid_order_reversal_bitwise():
+    """No work-group depends on another, so dispatching the work-groups in the
+    opposite order (FLASH_ATTN_REVERSE_ORDER=1, read per call) must give
+    bitwise the same O and LSE: causal, window with sinks, no mask, grouped
+    heads with ALiBi, a key split, the 8-wave kernel and the generic f32
+    kernel."""
+    cases = [
+        dict(shape=(2, 4, 1000, 128), dtype="bf16", kw=dict(causal=True)),
+        dict(shape=(2, 4, 1000, 128), dtype="bf16", kw=dict(causal=True, window=300, n_sink=4)),
+        dict(shape=(1, 8, 777, 64), dtype="f16", kw=dict(causal=False)),
+        dict(shape=(1, 8, 900, 128), dtype="bf16", kv=2, alibi=True, kw=dict(causal=True)),
+        dict(shape=(1, 4, 1500, 128), dtype="bf16", split=3, kw=dict(causal=True)),
+        dict(shape=(1, 64, 16384, 128), dtype="bf16", kw=dict(causal=True)),
+        dict(shape=(1, 2, 300, 32), dtype="f32", kw=dict(causal=True)),
+    ]
+    for c in cases:
+        B, H, S, D = c["shape"]
+        q, k, v = fa_inputs.make_qkv(B, H, S, D, c["dtype"], seed=8, H_kv=c.get("kv", 0))
+        qd, kd, vd = (t.cuda() for t in (q, k, v))
+        sl = torch.from_numpy(ORACLE.alibi_slopes(H).astype(np.float32)).cuda() \
+            if c.get("alibi") else None
+
+        def run():
+            if c.get("split"):
+                return fa.flash_attn_fwd_split(qd, kd, vd, n_split=c["split"], **c["kw"])
+            return fa.flash_attn_fwd(qd, kd, vd, alibi_slopes=sl, **c["kw"])
+
+        ref = run()
+        os.environ["FLASH_ATTN_REVERSE_ORDER"] = "1"
+        try:
+            rev = run()
+        finally:
+            del os.environ["FLASH_ATTN_REVERSE_ORDER"]
+        torch.cuda.synchronize()
+        _say(f"  reversed dispatch order {c['shape']} {c['dtype']} {c['kw']}: "
+             f"equal={torch.equal(ref[0], rev[0]) and torch.equal(ref[1], rev[1])}")
+        assert torch.equal(ref[0], rev[0]) and torch.equal(ref[1], rev[1]), c
 
 
 # --------------------------------------------------------------------------- #
