@@ -206,6 +206,33 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    float scale, const float* alibi_slopes, void* workspace,
                    int64_t workspace_bytes, void* stream, int dtype);
 
+/*
+ * flash_attn_bwd_noalloc -- flash_attn_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * The two per-row arrays flash_attn_bwd keeps in its workspace live instead in
+ * a static device array of the library, 32 MiB per GPU, held from the
+ * library's first use on that GPU until the process ends. The call allocates
+ * nothing and calls no allocating routine. Its limit: the workspace
+ * flash_attn_bwd would need, flash_attn_bwd_workspace_bytes(B, H, S), must be
+ * at most 32 MiB (8 bytes per row of B*H*S, S rounded up to a multiple of 128:
+ * about 4.19 million rows); larger shapes return FA_ERR_UNSUPPORTED.
+ *
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (from several streams or threads) race and must not be issued.
+ * Calls in sequence on a stream are safe; nothing of an earlier call's
+ * contents is read.
+ *
+ * Arguments, results, precision and the other errors are those of
+ * flash_attn_bwd; FA_ERR_HIP also reports a failure to look up the array.
+ */
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal,
+                           int64_t window, int64_t n_sink, float scale,
+                           const float* alibi_slopes, void* stream, int dtype);
+
 /* flash_attn_bwd_workspace_bytes -- host-only: bytes of flash_attn_bwd's
  * workspace for this shape, or -1 (flash_attn_last_error set) if invalid. */
 int64_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S);

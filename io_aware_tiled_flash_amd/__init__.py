@@ -12,7 +12,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_fwd_counted", "flash_attn_fwd_split",
+__all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_noalloc", "flash_attn_fwd_counted",
+           "flash_attn_fwd_split",
            "flash_attn_merge", "flash_attn_bwd_workspace_bytes",
            "flash_attn_split_workspace_bytes", "flash_attn_tile_shape",
            "flash_attn_last_error", "flash_attn_version", "capi", "library_path",
@@ -53,6 +54,10 @@ class _CAPI:
             "flash_attn_bwd",
             [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp,
              vp, i64, vp, i32], i32)
+        self.flash_attn_bwd_noalloc = self._fn(
+            "flash_attn_bwd_noalloc",
+            [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, f32, vp,
+             vp, i32], i32)
         self.flash_attn_bwd_workspace_bytes = self._fn(
             "flash_attn_bwd_workspace_bytes", [i64, i64, i64], i64)
         self.flash_attn_tile_shape = self._fn(
@@ -329,6 +334,28 @@ def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int =
             int(bool(causal)), int(window), int(n_sink), float(scale),
             None if alibi_slopes is None else alibi_slopes.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), stream, _dtype_code(q))
+    _check(rc)
+    return dq, dk, dv
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, *, causal: bool = False, window: int = 0,
+                           n_sink: int = 0, scale: float | None = None, alibi_slopes=None,
+                           dq=None, dk=None, dv=None):
+    """flash_attn_bwd with its per-row state in the library's static device
+    scratch instead of a workspace: the library call allocates nothing (pass
+    dq, dk, dv to allocate nothing here either). Shapes whose state exceeds
+    the scratch (B*H*S above about 4.19 million rows) raise NotImplementedError;
+    calls that overlap in time on one GPU race on the scratch."""
+    import torch
+    B, H, Hkv, S, D, scale, dq, dk, dv = _bwd_args(q, k, v, o, lse, dout, scale, alibi_slopes,
+                                                   dq, dk, dv)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = capi().flash_attn_bwd_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
+            int(bool(causal)), int(window), int(n_sink), float(scale),
+            None if alibi_slopes is None else alibi_slopes.data_ptr(), stream, _dtype_code(q))
     _check(rc)
     return dq, dk, dv
 

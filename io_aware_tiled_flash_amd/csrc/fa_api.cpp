@@ -141,6 +141,49 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   return err == hipSuccess ? FA_OK : launch_failed(err);
 }
 
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int causal,
+                           int64_t window, int64_t n_sink, float scale, const float* alibi_slopes,
+                           void* stream, int dtype) {
+  g_last_error.clear();
+  fa::BwdCall a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.S = S;
+  a.D = D;
+  a.causal = causal;
+  a.window = window;
+  a.n_sink = n_sink;
+  a.scale = scale;
+  a.alibi = alibi_slopes;
+  a.internal_workspace = true;
+  a.workspace_bytes = fa::kBwdScratchBytes;
+  a.dtype = dtype;
+  fa::BwdParams p;
+  const int rc = fa::prepare_bwd(a, &p, &g_last_error);
+  if (rc != FA_OK) return rc;
+  void* ws = nullptr;
+  hipError_t err = fa::bwd_scratch(&ws);
+  if (err != hipSuccess) {
+    g_last_error = std::string("scratch lookup failed: ") + hipGetErrorString(err);
+    return FA_ERR_HIP;
+  }
+  fa::bwd_bind_workspace(&p, ws);
+  err = fa::launch_bwd(p, (int)D, dtype, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FA_OK : launch_failed(err);
+}
+
 int64_t flash_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
   g_last_error.clear();
   return fa::bwd_workspace_bytes(B, H, S, &g_last_error);

@@ -24,6 +24,8 @@
 // of the forward kernel (16-byte chunks XOR-swizzled by row), which serves
 // both the row reads and the transposing reads without bank conflicts.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stdint.h>
 
 #include "fa_device.h"
@@ -623,6 +625,39 @@ FA_BWD_INST(_Float16, 64)
 #undef FA_BWD_INST
 
 static_assert(32 * kBwdWaves == kBwdRows && 2 * kBCf == kBwdRows, "tile sizes of the plan");
+
+// ------------------------------------------------------------------------ //
+// Scratch of the allocation-free backward: the two per-row arrays (delta and
+// lse * log2 e) of flash_attn_bwd_noalloc live in this file-scope device
+// array instead of a caller workspace. Every GPU the library runs on holds its
+// own copy until the process ends. Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and that address is what the kernels receive.
+// All calls on one GPU share the array; calls that overlap in time on one GPU
+// race on it. Nothing in it needs clearing: the dq kernel writes every padded
+// row before the dkv kernel reads it.
+// ------------------------------------------------------------------------ //
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+hipError_t bwd_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  constexpr int kMaxDevices = 64;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 template <typename T, int D, bool ALIBI>
 static hipError_t launch_bwd_a(const BwdParams& p, hipStream_t st) {

@@ -12,6 +12,9 @@ namespace fa {
 
 // Backward kernels: bf16 / f16 with D in {64, 128}.
 hipError_t launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t st);
+// Device address of the allocation-free backward's scratch array on the
+// current device (kBwdScratchBytes bytes; looked up once per device).
+hipError_t bwd_scratch(void** out);
 
 // Generic forward kernels: every dtype, D in {16, 32, 64, 128}.
 hipError_t launch_generic(const FwdParams& p, int D, int dtype, hipStream_t st);

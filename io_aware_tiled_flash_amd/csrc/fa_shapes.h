@@ -17,6 +17,9 @@ constexpr int kFastBC = 64;
 constexpr int kGenericBR = 128;
 constexpr int kGenericBC = 64;
 constexpr int kBwdRows = 128;
+// Size of the static device scratch of the allocation-free backward: the two
+// fp32 per-row arrays of 4M rows (B*H*S with S rounded up to kBwdRows).
+constexpr int64_t kBwdScratchBytes = (int64_t)32 << 20;
 
 inline bool fast_supported(int64_t D, int dtype) {
   return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);

@@ -268,7 +268,8 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, std::string* err) {
 
 int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   const int64_t B = a.B, H = a.H, H_kv = a.H_kv, S = a.S, D = a.D;
-  if (!a.q || !a.k || !a.v || !a.o || !a.dout || !a.lse || !a.dq || !a.dk || !a.dv || !a.workspace)
+  if (!a.q || !a.k || !a.v || !a.o || !a.dout || !a.lse || !a.dq || !a.dk || !a.dv ||
+      (!a.workspace && !a.internal_workspace))
     return fail(err, FA_ERR_INVALID, "null pointer");
   if (B < 1 || H < 1 || S < 1 || D < 1)
     return fail(err, FA_ERR_INVALID, "B, H, S and D must be >= 1");
@@ -297,20 +298,23 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   const uint64_t lb = (uint64_t)rows * 4;
   const int64_t need = bwd_workspace_bytes(B, H, S, err);
   if (need < 0) return FA_ERR_INVALID;
-  if (a.workspace_bytes < need) return fail(err, FA_ERR_INVALID, "workspace too small");
+  if (!a.internal_workspace && a.workspace_bytes < need)
+    return fail(err, FA_ERR_INVALID, "workspace too small");
   struct Region {
     const void* p;
     uint64_t n;
   };
-  const Region outs[] = {{a.dq, tb}, {a.dk, kvb}, {a.dv, kvb}, {a.workspace, (uint64_t)need}};
+  // (the library's scratch array is its own allocation and overlaps nothing)
+  const Region outs[] = {{a.dq, tb}, {a.dk, kvb}, {a.dv, kvb},
+                         {a.workspace, a.internal_workspace ? 0 : (uint64_t)need}};
   const Region ins[] = {{a.q, tb},    {a.k, kvb},   {a.v, kvb}, {a.o, tb},
                         {a.dout, tb}, {a.lse, lb}, {a.alibi, a.alibi ? (uint64_t)H * 4 : 0}};
   for (const Region& x : outs) {
     for (const Region& y : ins)
-      if (y.p && overlaps(x.p, x.n, y.p, y.n))
+      if (x.n && y.p && overlaps(x.p, x.n, y.p, y.n))
         return fail(err, FA_ERR_INVALID, "an output or the workspace overlaps an input");
     for (const Region& y : outs)
-      if (&x != &y && overlaps(x.p, x.n, y.p, y.n))
+      if (&x != &y && x.n && y.n && overlaps(x.p, x.n, y.p, y.n))
         return fail(err, FA_ERR_INVALID, "outputs overlap each other or the workspace");
   }
   if (!supported_d(D)) return fail(err, FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
@@ -321,6 +325,11 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   const int64_t nb = (S + br - 1) / br;
   if (S > INT32_MAX - 2 * br || B * H > INT32_MAX || nb * B * H > (int64_t)INT32_MAX / 256)
     return fail(err, FA_ERR_UNSUPPORTED, "S, B*H or the grid exceed the 32-bit index range");
+  if (a.internal_workspace && need > a.workspace_bytes)
+    return fail(err, FA_ERR_UNSUPPORTED,
+                "the allocation-free backward keeps at most 32 MiB of per-row state "
+                "(8 bytes per row of B*H*S, S rounded up to 128): use flash_attn_bwd "
+                "with a workspace");
 
   BwdParams& p = *out;
   p.q = a.q;

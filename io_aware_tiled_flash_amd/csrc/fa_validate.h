@@ -63,6 +63,11 @@ struct BwdCall {
   void* workspace = nullptr;
   int64_t workspace_bytes = 0;
   int dtype = 0;
+  // The library's own scratch array holds the per-row state instead of a
+  // caller workspace (the allocation-free entry point): the workspace pointer
+  // is then bound after validation, and workspace_bytes is the array's size;
+  // a shape that needs more is FA_ERR_UNSUPPORTED.
+  bool internal_workspace = false;
 };
 
 int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err);

@@ -251,6 +251,40 @@ int main() {
   bwd_case("f32", FA_ERR_UNSUPPORTED, [](fa::BwdCall& a) { a.dtype = FA_F32; });
   bwd_case("d32", FA_ERR_UNSUPPORTED, [](fa::BwdCall& a) { a.D = 32; });
   bwd_case("window_no_causal", FA_ERR_INVALID, [](fa::BwdCall& a) { a.causal = 0; a.window = 4; });
+  // the library's own scratch (no workspace pointer): valid within its size,
+  // FA_ERR_UNSUPPORTED past it, and the workspace binds afterwards
+  bwd_case("internal_ws", FA_OK, [](fa::BwdCall& a) {
+    a.workspace = nullptr;
+    a.internal_workspace = true;
+    a.workspace_bytes = fa::kBwdScratchBytes;
+  });
+  bwd_case("internal_ws_too_big", FA_ERR_UNSUPPORTED, [](fa::BwdCall& a) {
+    a.workspace = nullptr;
+    a.internal_workspace = true;
+    a.workspace_bytes = fa::kBwdScratchBytes;
+    a.H = 2050;
+    a.H_kv = 2050;
+    a.S = 2048;
+    for (const void** t : {&a.q, &a.k, &a.v, &a.o, &a.dout})
+      *t = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(*t) << 20);
+    a.lse = reinterpret_cast<const float*>(reinterpret_cast<uintptr_t>(a.lse) << 20);
+    for (void** t : {&a.dq, &a.dk, &a.dv})
+      *t = reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(*t) << 20);
+  });
+  {
+    fa::BwdCall a = base_bwd();
+    a.workspace = nullptr;
+    a.internal_workspace = true;
+    a.workspace_bytes = fa::kBwdScratchBytes;
+    fa::BwdParams p;
+    std::string err;
+    expect(fa::prepare_bwd(a, &p, &err) == FA_OK && p.delta == nullptr && p.lse2 == nullptr,
+           "internal workspace unbound after validation");
+    fa::bwd_bind_workspace(&p, addr<void>(0x40000000));
+    expect(p.delta == addr<float>(0x40000000) &&
+               p.lse2 == addr<float>(0x40000000) + (int64_t)p.BH * p.Sp && p.Sp == 128,
+           "internal workspace bound");
+  }
 
   // ---- merge and sizes ----
   {

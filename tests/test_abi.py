@@ -306,3 +306,47 @@ def test_bwd_workspace_bytes():
     assert fa.capi().flash_attn_bwd_workspace_bytes(1, 1, 129) == (2 * 256 * 4 + 255) // 256 * 256
     assert fa.capi().flash_attn_bwd_workspace_bytes(0, 3, 100) == -1
 
+
+# --------------------------------------------------------------------------- #
+# Allocation-free backward: same validation, then the size limit of the
+# library's scratch (all of this fails before any HIP call)
+# --------------------------------------------------------------------------- #
+
+def _call_bwd_noalloc(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, B=1, H=2, H_kv=2,
+                      S=64, D=64, causal=1, window=0, n_sink=0, scale=0.125, alibi=None,
+                      dtype=fa.FA_BF16):
+    rc = fa.capi().flash_attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, S, D,
+                                          causal, window, n_sink, scale, alibi, None, dtype)
+    return rc, fa.flash_attn_last_error()
+
+
+INVALID_BWD_NOALLOC = {k: v for k, v in INVALID_BWD.items()
+                       if k not in ("null_workspace", "workspace_small", "workspace_overlaps_dq")}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID_BWD_NOALLOC))
+def test_invalid_bwd_noalloc_arguments_rejected(case):
+    rc, msg = _call_bwd_noalloc(**INVALID_BWD_NOALLOC[case])
+    assert rc == fa.FA_ERR_INVALID, (case, rc, msg)
+    assert msg
+
+
+def test_bwd_noalloc_size_limit():
+    """The scratch holds 32 MiB: 8 bytes per padded row of B*H*S. One row past
+    it is rejected with a message naming the way out (a caller workspace);
+    tensors are placed far apart so that only the limit is in question."""
+    far = 1 << 40
+    ptrs = dict(q=1 * far, k=2 * far, v=3 * far, o=4 * far, dout=5 * far, lse=6 * far,
+                dq=7 * far, dk=8 * far, dv=9 * far)
+    rows_max = (32 << 20) // 8            # 4,194,304 padded rows
+    H = rows_max // 4096 + 1              # B*H*4096 rows, one head too many
+    rc, msg = _call_bwd_noalloc(**ptrs, B=1, H=H, H_kv=H, S=4096, D=128)
+    assert rc == fa.FA_ERR_UNSUPPORTED and "flash_attn_bwd" in msg, (rc, msg)
+    assert fa.capi().flash_attn_bwd_workspace_bytes(1, H, 4096) > (32 << 20)
+    assert fa.capi().flash_attn_bwd_workspace_bytes(1, H - 1, 4096) <= (32 << 20)
+
+
+def test_bwd_noalloc_unsupported_types():
+    for kw in (dict(dtype=fa.FA_F32), dict(D=32)):
+        rc, msg = _call_bwd_noalloc(**kw)
+        assert rc == fa.FA_ERR_UNSUPPORTED, (kw, msg)
