@@ -110,7 +110,9 @@ struct Core {
     l_run = 0.f;
     c = (AL == 2) ? 1.f : p.c;
     beta = (AL == 1) ? b2 / p.c : 0.f;
-    tau_raw = kTau / c;
+    // (clamped: at the smallest scales kTau / c overflows, and -inf + inf
+    // would keep the reference at -inf for good)
+    tau_raw = fminf(kTau / c, 3.402823466e+38f);
   }
 
   // S^T = K Q^T for the K tile at ks. The two 32-key sub-tiles alternate
@@ -457,6 +459,177 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
     core.epilogue(p, head, bh);
 }
 
+// ------------------------------------------------------------------------ //
+// Key-halves schedule for grids too small to fill the chip (fewer than two
+// 4-wave work-groups per CU): 8 waves per work-group of 128 query rows, in
+// two halves of four. Wave w covers rows 32 (w & 3) .. +31 like the 4-wave
+// kernel, and half w >> 2 streams its own contiguous half of the query
+// block's key blocks through its own double-buffered K/V tiles, so every
+// SIMD holds two waves and each wave takes half the steps. At the end the
+// halves combine their (max, sum, O) row by row through LDS -- the same
+// rescale the online softmax applies between blocks -- and the first half
+// writes the result.
+// ------------------------------------------------------------------------ //
+template <typename T, int D>
+__device__ __forceinline__ void fwd_halves_body(const FwdParams& p, T* (&kbuf)[4], T* (&vbuf)[4]) {
+  constexpr int BR = 128;
+  constexpr int BC = kBCf;
+  using C = Core<T, D, BR, 0>;
+  static_assert(C::NT == 2, "four 16-key chunks per block");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave & 3;      // row block of the wave
+  const int half = wave >> 2;   // key half of the wave
+
+  int qb, bh;
+  wg_coords(p, wg_id(p), qb, bh);
+  const int S = p.S;
+  const int q_lo = qb * BR;
+  const size_t head = (size_t)bh * (size_t)S * D;
+  const size_t kv_head = (size_t)(bh / p.G) * (size_t)S * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
+  const T* __restrict__ Kh = uniform_ptr(reinterpret_cast<const T*>(p.k) + kv_head);
+  const T* __restrict__ Vh = uniform_ptr(reinterpret_cast<const T*>(p.v) + kv_head);
+
+  const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
+  const int n_all = br.count();
+  const int n_first = (n_all + 1) / 2;   // the first half takes the odd block
+  const int steps = n_first;             // both halves run this many steps
+  if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_all);
+
+  C core;
+  core.init(p, Qh, q_lo + 32 * rw + (lane & 31), lane, bh);
+
+  // Half HALF: blocks [it_b, it_b + n_iter) of the query block, tiles in
+  // kbuf/vbuf[2 HALF + parity].
+  auto run = [&](auto half_c) __attribute__((always_inline)) {
+    constexpr int HALF = decltype(half_c)::value;
+    const int it_b = HALF ? n_first : 0;
+    const int n_iter = HALF ? n_all - n_first : n_first;
+    auto kb = [&](int t) __attribute__((always_inline)) { return br.kb(it_b + t); };
+    T* const k0s = kbuf[2 * HALF];
+    T* const k1s = kbuf[2 * HALF + 1];
+    T* const v0s = vbuf[2 * HALF];
+    T* const v1s = vbuf[2 * HALF + 1];
+    TileDma<T, D, 4, false> kdma;
+    TileDma<T, D, 4, true> vdma;
+    kdma.init(rw, lane);
+    vdma.init(rw, lane);
+    if (n_iter > 0) {
+      kdma.load(k0s, Kh, kb(0) * BC, S, rw);
+      vdma.load(v0s, Vh, kb(0) * BC, S, rw);
+    }
+    wait_vmem<0>();
+    __syncthreads();
+    auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr bool MASK = decltype(mask)::value;
+      T* kc = PAR == 0 ? k0s : k1s;
+      T* vc = PAR == 0 ? v0s : v1s;
+      T* kn = PAR == 0 ? k1s : k0s;
+      T* vn = PAR == 0 ? v1s : v0s;
+      if (it + 1 < n_iter) {
+        const int k1 = kb(it + 1) * BC;
+        kdma.load(kn, Kh, k1, S, rw);
+        vdma.load(vn, Vh, k1, S, rw);
+      }
+      const int k0 = kb(it) * BC;
+      if (!MASK || !block_hidden<BC>(q_lo + 32 * rw, q_lo + 32 * rw + 31, k0, p.causal, p.window,
+                                     p.n_sink)) {
+        f32x16 sacc[C::NT];
+        core.qk(sacc, kc);
+        if (MASK) core.mask(sacc, p, k0);
+        core.max_update(sacc, 0.f);
+        typename C::v8 pb[4];
+        core.l_run = core.exp_block(sacc, pb, core.bias(0.f));
+        core.pv(vc, pb);
+      }
+      wait_vmem<0>();
+      __syncthreads();
+    };
+    auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
+      int it = b;
+      if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+      for (; it + 2 <= e; it += 2) {
+        step(std::integral_constant<int, 0>{}, mask, it);
+        step(std::integral_constant<int, 1>{}, mask, it + 1);
+      }
+      if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+    };
+    int f0 = 0;
+    while (f0 < n_iter && !block_full<BR, BC>(q_lo, kb(f0) * BC, S, p.causal, p.window, p.n_sink))
+      ++f0;
+    int f1 = f0;
+    while (f1 < n_iter && block_full<BR, BC>(q_lo, kb(f1) * BC, S, p.causal, p.window, p.n_sink))
+      ++f1;
+    segment(std::true_type{}, 0, f0);
+    segment(std::false_type{}, f0, f1);
+    segment(std::true_type{}, f1, n_iter);
+    // a shorter half meets the longer one's barriers
+    for (int it = n_iter; it < steps; ++it) __syncthreads();
+  };
+  if (half == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+
+  // Combine the halves: the second half's O, reference max and sum go
+  // through LDS (the tile buffers are idle now), lane by lane: a lane of the
+  // partner wave holds the same rows and columns of O^T. Row block rw stages
+  // its O in K tile buffer rw and its three per-lane numbers in a slice of
+  // the first V tile buffer.
+  constexpr int NO = C::NDT * 16;   // O values per lane
+  static_assert(NO * 64 * sizeof(float) <= kBCf * D * sizeof(T), "one wave's O fits a tile");
+  static_assert(4 * 3 * 64 * sizeof(float) <= kBCf * D * sizeof(T), "the row numbers fit a tile");
+  T* const kst = rw == 0 ? kbuf[0] : rw == 1 ? kbuf[1] : rw == 2 ? kbuf[2] : kbuf[3];
+  float* const ostage = reinterpret_cast<float*>(kst);
+  float* const sstage = reinterpret_cast<float*>(vbuf[0]) + rw * 3 * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ostage[(dt * 16 + r) * 64 + lane] = core.oacc[dt][r];
+    sstage[lane] = core.m_run;
+    sstage[64 + lane] = core.mc;
+    sstage[128 + lane] = core.l_run;
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float m1 = sstage[lane], mc1 = sstage[64 + lane], l1 = sstage[128 + lane];
+    const bool e0 = core.m_run == kNegInf, e1 = m1 == kNegInf;
+    const float m = e0 ? mc1 : (e1 ? core.mc : fmaxf(core.mc, mc1));
+    const float a0 = e0 ? 0.f : fast_exp2(core.mc - m);
+    const float a1 = e1 ? 0.f : fast_exp2(mc1 - m);
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        core.oacc[dt][r] = core.oacc[dt][r] * a0 + ostage[(dt * 16 + r) * 64 + lane] * a1;
+    core.l_run = core.l_run * a0 + l1 * a1;
+    core.mc = m;
+    core.epilogue(p, head, bh);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_halves_kernel(FwdParams p) {
+  constexpr int TILE = kBCf * D;
+  __shared__ __attribute__((aligned(1024))) T k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k2s[TILE];
+  __shared__ __attribute__((aligned(1024))) T k3s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v1s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v2s[TILE];
+  __shared__ __attribute__((aligned(1024))) T v3s[TILE];
+  T* kbuf[4] = {k0s, k1s, k2s, k3s};
+  T* vbuf[4] = {v0s, v1s, v2s, v3s};
+  fwd_halves_body<T, D>(p, kbuf, vbuf);
+}
+
 template <typename T, int D, int NW, int AL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fast_kernel(FwdParams p) {
@@ -501,12 +674,20 @@ FA_FAST_INST(_Float16, 128, 4)
 FA_FAST_INST(_Float16, 64, 8)
 FA_FAST_INST(_Float16, 64, 4)
 #undef FA_FAST_INST
+template __global__ void fa_fwd_halves_kernel<__bf16, 128>(FwdParams);
+template __global__ void fa_fwd_halves_kernel<__bf16, 64>(FwdParams);
+template __global__ void fa_fwd_halves_kernel<_Float16, 128>(FwdParams);
+template __global__ void fa_fwd_halves_kernel<_Float16, 64>(FwdParams);
 
 
 
 template <typename T, int D, int AL>
 static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH * (unsigned)p.n_split;
+  if (AL == 0 && p.halves) {
+    hipLaunchKernelGGL((fa_fwd_halves_kernel<T, D>), dim3(grid), dim3(512), 0, st, p);
+    return;
+  }
   if (nw == 8)
     hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, AL>), dim3(grid), dim3(512), 0, st, p);
   else

@@ -52,6 +52,7 @@ struct FwdParams {
   float c;      // |scale| * log2(e), at least FLT_MIN
   int neg;      // scale < 0
   int reverse;  // 1: work-groups take their tiles in reverse dispatch order (testing aid)
+  int halves;   // 1: the fast kernel's key-halves schedule (8 waves, small grids)
 };
 
 // Arguments of one backward launch (validated on the host). c = scale * log2(e)

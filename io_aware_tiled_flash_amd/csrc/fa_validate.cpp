@@ -205,6 +205,14 @@ int prepare_fwd(const FwdCall& a, FwdLaunch* out, std::string* err) {
   p.c = cf;
   p.neg = a.scale < 0.f ? 1 : 0;
   p.reverse = reverse_order();
+  // Grids of fewer than two 4-wave work-groups per CU (256 CUs) take the
+  // key-halves schedule (no ALiBi, no key split): two waves on every SIMD,
+  // each with half the key blocks. FLASH_ATTN_HALVES=0|1 overrides (tuning).
+  p.halves = plan.fast && plan.nw == 4 && !a.alibi && n_split == 1 && nqb * bh < 512;
+  if (const char* e = std::getenv("FLASH_ATTN_HALVES")) {
+    if (e[0] == '0') p.halves = 0;
+    if (e[0] == '1') p.halves = plan.fast && plan.nw == 4 && !a.alibi && n_split == 1;
+  }
   out->plan = plan;
   out->rows = rows;
   return FA_OK;

@@ -462,6 +462,29 @@ def test_grid_order_reversal_bitwise():
         assert torch.equal(ref[0], rev[0]) and torch.equal(ref[1], rev[1]), c
 
 
+@pytest.mark.parametrize("halves", ["0", "1"])
+@pytest.mark.parametrize("dtype, D", [("bf16", 128), ("f16", 64)])
+def test_both_small_grid_schedules(halves, dtype, D):
+    """Grids of fewer than 512 work-groups take the key-halves schedule by
+    default (no ALiBi, no key split); FLASH_ATTN_HALVES=0|1, read per call,
+    forces either schedule. Both against the oracle: the 4-wave kernel keeps
+    its small-size coverage, and the key-halves kernel meets a half with no
+    visible key (one key block, a narrow window), an odd block count and
+    ragged tails."""
+    os.environ["FLASH_ATTN_HALVES"] = halves
+    try:
+        for S in (1, 64, 65, 129, 700, 1000):
+            q, k, v = fa_inputs.make_qkv(1, 2, S, D, dtype, seed=S + 11 * D)
+            for causal, window, n_sink in MASKS:
+                scale = 1.0 / math.sqrt(D)
+                o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
+                compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
+                        n_sink=n_sink,
+                        label=f"halves={halves} {dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
+    finally:
+        del os.environ["FLASH_ATTN_HALVES"]
+
+
 # --------------------------------------------------------------------------- #
 # Block skipping: the instrumentation counter against a count from the mask
 # --------------------------------------------------------------------------- #

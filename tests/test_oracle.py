@@ -658,9 +658,10 @@ def test_planted_mistake_is_caught(name):
 
 
 def test_lab3_fp16_study():
-    """Lab 3, exercise 5: switch both versions to float16 and compare their
-    errors. On one head shaped like the SDPA example ([2, 8, 1024, 64], fp16,
-    no mask, scale 1/8), the materialised formula and the tiled fold are run
+    """Lab 3, exercise 5 asks for the two versions (materialised and tiled)
+    in half precision, with their errors compared. On one head shaped like the
+    SDPA example ([2, 8, 1024, 64], fp16, no mask, scale 1/8), the
+    materialised formula and the tiled fold are run
     with every step in NumPy float16 and compared with the fp64 oracle on the
     same (fp16-valued) inputs. The page prints no value, so this is a study,
     parity unpinned: the test records both errors and only requires them to be
