@@ -162,11 +162,13 @@ __device__ __forceinline__ void wg_coords(const FwdParams& p, int& qb, int& bh) 
 // ALiBi bias in the base-2 logit domain: turns raw (sign-folded) scores into
 // t = c * s - b2 * |i - j| for keys j = jb + e, e = 32 t + 8 (r >> 2) + (r & 3),
 // with b2 = slope * log2(e). The softmax then runs on t with a unit scale.
-template <int NT>
+// Only the first NTU of the NT sub-tiles are touched.
+template <int NTU, int NT>
 __device__ __forceinline__ void alibi_logits(f32x16 (&acc)[NT], float c, float b2, int i, int jb) {
+  static_assert(NTU <= NT, "sub-tiles");
   const float d0 = (float)(i - jb);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NTU; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float e = (float)(32 * t + 8 * (r >> 2) + (r & 3));
@@ -179,10 +181,11 @@ __device__ __forceinline__ void alibi_logits(f32x16 (&acc)[NT], float c, float b
 // beta = slope log2(e) / c and key j = jb + 4h + e. This adds the per-key part beta e (e a compile-time
 // constant, one FMA per score); the per-row part beta (jb + 4h - i) is one
 // number per lane and block, applied in the softmax.
-template <int NT>
+template <int NTU, int NT>
 __device__ __forceinline__ void alibi_ramp(f32x16 (&acc)[NT], float beta) {
+  static_assert(NTU <= NT, "sub-tiles");
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NTU; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       acc[t][r] = __builtin_fmaf((float)(32 * t + 8 * (r >> 2) + (r & 3)), beta, acc[t][r]);

@@ -119,27 +119,30 @@ struct Core {
   // (independent accumulators back to back), and the K fragment reads run
   // kQkAhead MFMAs ahead of their use: left to itself the scheduler keeps only
   // one or two reads in flight, and each MFMA then waits out an LDS latency.
+  // NTU < NT: only the first NTU sub-tiles (the rest of the block is known
+  // to be hidden); the same holds for mask, max_update, exp_block and pv.
   static constexpr int kQkAhead = 4;
+  template <int NTU = NT>
   __device__ __forceinline__ void qk(f32x16 (&acc)[NT], const T* ks) const {
-    v8 a[NS][NT];
+    v8 a[NS][NTU];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NTU; ++t)
         a[s][t] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(ks + 32 * t * D + koff[s]));
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NTU; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = Tr::mma(a[s][t], qf[s], acc[t]);
+      for (int t = 0; t < NTU; ++t) acc[t] = Tr::mma(a[s][t], qf[s], acc[t]);
     // Schedule: kQkAhead reads, then (one MFMA, one read) pairs, then the
     // last MFMAs. Mask bits: 0x100 LDS read, 0x008 MFMA.
     __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
 #pragma unroll
-    for (int u = 0; u < NS * NT - kQkAhead; ++u) {
+    for (int u = 0; u < NS * NTU - kQkAhead; ++u) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -148,6 +151,7 @@ struct Core {
 
   // Mask the scores of a partially visible block: key j = k0 + 4h + e,
   // e = 32t + 8g + r.
+  template <int NTU = NT>
   __device__ __forceinline__ void mask(f32x16 (&acc)[NT], const FwdParams& p, int k0) const {
     const int jb = k0 + 4 * h;
     const int hi = (p.causal ? min(i, p.S - 1) : p.S - 1) - jb;
@@ -155,7 +159,7 @@ struct Core {
       const int lo = i - p.window + 1 - jb;
       const int sk = p.n_sink - 1 - jb;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NTU; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int e = 32 * t + 8 * (r >> 2) + (r & 3);
@@ -164,7 +168,7 @@ struct Core {
         }
     } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NTU; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int e = 32 * t + 8 * (r >> 2) + (r & 3);
@@ -180,6 +184,7 @@ struct Core {
   // l are then rescaled. The decision is wave-uniform, so the rescale is
   // skipped as a branch. off (AL == 1 only): this lane's ALiBi offset for the
   // block (see alibi_ramp).
+  template <int NTU = NT>
   __device__ __forceinline__ void max_update(const f32x16 (&acc)[NT], float off) {
     // Sub-tile 0: the reference and 16 scores (8 v_maximum3); later
     // sub-tiles: 15 scores (7), their 16th joins the final maximum3. With
@@ -188,7 +193,7 @@ struct Core {
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mj = vmax(vmax(mj, acc[0][r]), acc[0][r + 1]);
 #pragma unroll
-    for (int t = 1; t < NT; ++t) {
+    for (int t = 1; t < NTU; ++t) {
       float a = vmax(vmax(acc[t][0], acc[t][1]), acc[t][2]);
 #pragma unroll
       for (int r = 3; r < 15; r += 2) a = vmax(vmax(a, acc[t][r]), acc[t][r + 1]);
@@ -237,26 +242,33 @@ struct Core {
 
   // The weights of the whole block; returns l_run plus their sum (four add
   // chains, one of them starting from l_run).
+  template <int NTU = NT>
   __device__ __forceinline__ float exp_block(f32x16 (&acc)[NT], v8 (&pb)[4], float bo) const {
+    static_assert(NT == 2 && (NTU == 1 || NTU == 2), "two 32-key sub-tiles");
     float ls[4] = {l_run, 0.f, 0.f, 0.f};
     exp_chunk<0>(acc, pb[0], bo, ls);
     exp_chunk<1>(acc, pb[1], bo, ls);
-    exp_chunk<2>(acc, pb[2], bo, ls);
-    exp_chunk<3>(acc, pb[3], bo, ls);
+    if constexpr (NTU == 2) {
+      exp_chunk<2>(acc, pb[2], bo, ls);
+      exp_chunk<3>(acc, pb[3], bo, ls);
+    }
     return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   }
 
   // O^T += V^T P^T for the V tile at vs, chunk by chunk.
+  template <int NTU = NT>
   __device__ __forceinline__ void pv(const T* vs, const v8 (&pb)[4]) {
     u32x4 vf[NDT];
     v_read<0>(vs, vf);
     pv_chunk(vf, pb[0]);
     v_read<1>(vs, vf);
     pv_chunk(vf, pb[1]);
-    v_read<2>(vs, vf);
-    pv_chunk(vf, pb[2]);
-    v_read<3>(vs, vf);
-    pv_chunk(vf, pb[3]);
+    if constexpr (NTU == 2) {
+      v_read<2>(vs, vf);
+      pv_chunk(vf, pb[2]);
+      v_read<3>(vs, vf);
+      pv_chunk(vf, pb[3]);
+    }
   }
 
   // V^T fragments of chunk TU for every d tile: two transposing reads each.
@@ -403,9 +415,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
   // puts a branch between the two; measured on the causal B4 H16 S4096 D128
   // workload, that ran 4 % slower.)
   static_assert(C::NT == 2, "four 16-key chunks per block");
-  auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
+  // NTU: 32-key sub-tiles computed (1 only for a sink block whose visible
+  // keys all lie in its first 32).
+  auto step = [&](auto par, auto mask, int it, auto ntu_c) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     constexpr bool MASK = decltype(mask)::value;
+    constexpr int NTU = decltype(ntu_c)::value;
     T* kc = PAR == 0 ? k0s : k1s;
     T* vc = PAR == 0 ? v0s : v1s;
     T* kn = PAR == 0 ? k1s : k0s;
@@ -421,28 +436,29 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
     if (!MASK || !block_hidden<BC>(q_lo + 32 * wave, q_lo + 32 * wave + 31, k0, p.causal,
                                    p.window, p.n_sink)) {
       f32x16 sacc[C::NT];
-      core.qk(sacc, kc);
-      if (MASK) core.mask(sacc, p, k0);
-      if (AL == 2) alibi_logits<C::NT>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
-      if (AL == 1) alibi_ramp<C::NT>(sacc, core.beta);
+      core.template qk<NTU>(sacc, kc);
+      if (MASK) core.template mask<NTU>(sacc, p, k0);
+      if (AL == 2) alibi_logits<NTU>(sacc, p.c, core.b2, core.i, k0 + 4 * core.h);
+      if (AL == 1) alibi_ramp<NTU>(sacc, core.beta);
       const float off = AL == 1 ? core.beta * (float)(k0 + 4 * core.h - core.i) : 0.f;
-      core.max_update(sacc, off);
+      core.template max_update<NTU>(sacc, off);
       typename C::v8 pb[4];
-      core.l_run = core.exp_block(sacc, pb, core.bias(off));
-      core.pv(vc, pb);
+      core.l_run = core.template exp_block<NTU>(sacc, pb, core.bias(off));
+      core.template pv<NTU>(vc, pb);
     }
     wait_vmem<0>();
     __syncthreads();
   };
+  using Full = std::integral_constant<int, C::NT>;
   // Steps [b, e) of one segment; the buffer pair alternates with it & 1.
   auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
     int it = b;
-    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++, Full{});
     for (; it + 2 <= e; it += 2) {
-      step(std::integral_constant<int, 0>{}, mask, it);
-      step(std::integral_constant<int, 1>{}, mask, it + 1);
+      step(std::integral_constant<int, 0>{}, mask, it, Full{});
+      step(std::integral_constant<int, 1>{}, mask, it + 1, Full{});
     }
-    if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+    if (it < e) step(std::integral_constant<int, 0>{}, mask, it, Full{});
   };
   int f0 = 0;
   while (f0 < n_iter && !block_full<BR, BC>(q_lo, kb(f0) * BC, S, p.causal, p.window, p.n_sink))
@@ -450,7 +466,17 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
   int f1 = f0;
   while (f1 < n_iter && block_full<BR, BC>(q_lo, kb(f1) * BC, S, p.causal, p.window, p.n_sink))
     ++f1;
-  segment(std::true_type{}, 0, f0);
+  // A walk that starts with the sink block (a window whose first block lies
+  // past it) sees in that block only the keys below n_sink; with at most 32
+  // sinks its second sub-tile is hidden, so that step computes half a block.
+  // (The backwards ALiBi walk reaches the sink block last; it keeps the full
+  // step.)
+  int s0 = 0;
+  if (AL != 1 && it_b == 0 && br.n_sinkb == 1 && p.n_sink <= 32 && f0 > 0) {
+    step(std::integral_constant<int, 0>{}, std::true_type{}, 0, std::integral_constant<int, 1>{});
+    s0 = 1;
+  }
+  segment(std::true_type{}, s0, f0);
   segment(std::false_type{}, f0, f1);
   segment(std::true_type{}, f1, n_iter);
   if (p.o_part)

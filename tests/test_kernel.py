@@ -470,12 +470,14 @@ def test_both_small_grid_schedules(halves, dtype, D):
     forces either schedule. Both against the oracle: the 4-wave kernel keeps
     its small-size coverage, and the key-halves kernel meets a half with no
     visible key (one key block, a narrow window), an odd block count and
-    ragged tails."""
+    ragged tails. Sink counts 32 and 33 straddle the 4-wave kernel's
+    half-width sink step (taken when every sink lies in the first 32 keys of
+    the sink block)."""
     os.environ["FLASH_ATTN_HALVES"] = halves
     try:
         for S in (1, 64, 65, 129, 700, 1000):
             q, k, v = fa_inputs.make_qkv(1, 2, S, D, dtype, seed=S + 11 * D)
-            for causal, window, n_sink in MASKS:
+            for causal, window, n_sink in MASKS + [(True, 200, 32), (True, 200, 33)]:
                 scale = 1.0 / math.sqrt(D)
                 o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
                 compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
