@@ -135,21 +135,53 @@ def _check_workspace(t, device, need: int):
         raise ValueError(f"workspace must hold at least {need} bytes")
 
 
+_codes = None
+_raw_stream = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
-    if t.dtype not in codes:
+    global _codes
+    if _codes is None:
+        import torch
+        _codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    code = _codes.get(t.dtype)
+    if code is None:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    return codes[t.dtype]
+    return code
+
+
+def _stream_handle(index: int) -> int:
+    """Handle of torch's current stream on device `index` (the caller has
+    made that device current). torch's raw-stream query returns the handle
+    without building a Stream object; the public call is the fallback."""
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+        fn = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = fn if fn is not None else (
+            lambda i: torch.cuda.current_stream(i).cuda_stream)
+    return _raw_stream(index)
+
+
+def _on_device(index: int, call):
+    """Run call() with device `index` current (switching only when another
+    device is current)."""
+    import torch
+    if torch.cuda.current_device() == index:
+        return call()
+    with torch.cuda.device(index):
+        return call()
 
 
 def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alibi_slopes=None,
              n_split=None, workspace=None):
     import torch
+    # (device checks compare get_device() indices: -1 for a host tensor)
+    Tensor = torch.Tensor
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+        if not isinstance(t, Tensor) or t.dim() != 4:
             raise ValueError(f"{name} must be a 4-D torch tensor [B, H, S, D]")
-        if not t.is_cuda:
+        if t.get_device() < 0:
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous [B, H, S, D]")
@@ -159,54 +191,62 @@ def _forward(q, k, v, causal, window, n_sink, scale, out, lse, block_pairs, alib
         raise ValueError("k and v must be [B, H_kv, S, D] with q's B, S, D")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype")
-    if k.device != q.device or v.device != q.device:
+    dev = q.get_device()
+    if k.get_device() != dev or v.get_device() != dev:
         raise ValueError("q, k, v must be on one device")
     if alibi_slopes is not None:
-        if not isinstance(alibi_slopes, torch.Tensor) or alibi_slopes.dtype != torch.float32 \
+        if not isinstance(alibi_slopes, Tensor) or alibi_slopes.dtype != torch.float32 \
                 or alibi_slopes.shape != (H,) or not alibi_slopes.is_contiguous() \
-                or alibi_slopes.device != q.device:
+                or alibi_slopes.get_device() != dev:
             raise ValueError("alibi_slopes must be a contiguous float32 tensor [H] on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
-    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+    if not isinstance(o, Tensor) or o.shape != q.shape or o.dtype != q.dtype \
+            or not o.is_contiguous() or o.get_device() != dev:
         raise ValueError("out must be a contiguous tensor like q")
-    if l.shape != (B, H, S) or l.dtype != torch.float32 or not l.is_contiguous() \
-            or l.device != q.device:
+    if not isinstance(l, Tensor) or l.shape != (B, H, S) or l.dtype != torch.float32 \
+            or not l.is_contiguous() or l.get_device() != dev:
         raise ValueError("lse must be a contiguous float32 tensor [B, H, S] on q's device")
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr())
-        mask = (int(bool(causal)), int(window), int(n_sink), float(scale))
-        if n_split is not None:
-            need = capi().flash_attn_split_workspace_bytes(B, H, S, D, int(n_split))
-            if need < 0:
-                _check(FA_ERR_INVALID)
-            if workspace is None and need > 0:
-                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-            elif workspace is not None:
-                _check_workspace(workspace, q.device, need)
-            ws_ptr = None if workspace is None else workspace.data_ptr()
-            ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-            slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
-            rc = capi().flash_attn_fwd_split(*ptrs, B, H, Hkv, S, D, *mask, slopes, int(n_split),
-                                             ws_ptr, ws_bytes, stream, _dtype_code(q))
-        elif Hkv != H or alibi_slopes is not None:
-            if block_pairs is not None:
-                raise ValueError("the block counter is available for plain multi-head calls only")
-            slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
-            rc = capi().flash_attn_fwd_ext(*ptrs, B, H, Hkv, S, D, *mask, slopes, stream,
-                                           _dtype_code(q))
-        elif block_pairs is None:
-            rc = capi().flash_attn_fwd(*ptrs, B, H, S, D, *mask, stream, _dtype_code(q))
-        else:
-            if block_pairs.dtype not in (torch.int64, torch.uint64) or block_pairs.numel() < 1 \
-                    or not block_pairs.is_cuda:
-                raise ValueError("block_pairs must be a GPU int64 tensor")
-            rc = capi().flash_attn_fwd_counted(*ptrs, B, H, S, D, *mask, stream, _dtype_code(q),
-                                               block_pairs.data_ptr())
-    _check(rc)
+    code = _dtype_code(q)
+    mask = (int(bool(causal)), int(window), int(n_sink), float(scale))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr())
+    slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+    lib = capi()
+    if n_split is not None:
+        need = lib.flash_attn_split_workspace_bytes(B, H, S, D, int(n_split))
+        if need < 0:
+            _check(FA_ERR_INVALID)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif workspace is not None:
+            _check_workspace(workspace, q.device, need)
+        ws_ptr = None if workspace is None else workspace.data_ptr()
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+        def call():
+            return lib.flash_attn_fwd_split(*ptrs, B, H, Hkv, S, D, *mask, slopes, int(n_split),
+                                            ws_ptr, ws_bytes, _stream_handle(dev), code)
+    elif Hkv != H or alibi_slopes is not None:
+        if block_pairs is not None:
+            raise ValueError("the block counter is available for plain multi-head calls only")
+
+        def call():
+            return lib.flash_attn_fwd_ext(*ptrs, B, H, Hkv, S, D, *mask, slopes,
+                                          _stream_handle(dev), code)
+    elif block_pairs is None:
+        def call():
+            return lib.flash_attn_fwd(*ptrs, B, H, S, D, *mask, _stream_handle(dev), code)
+    else:
+        if not isinstance(block_pairs, Tensor) or block_pairs.dtype not in (torch.int64, torch.uint64) \
+                or block_pairs.numel() < 1 or block_pairs.get_device() != dev:
+            raise ValueError("block_pairs must be an int64 tensor on q's device")
+
+        def call():
+            return lib.flash_attn_fwd_counted(*ptrs, B, H, S, D, *mask, _stream_handle(dev), code,
+                                              block_pairs.data_ptr())
+    _check(_on_device(dev, call))
     return o, l
 
 
@@ -267,11 +307,11 @@ def flash_attn_merge(o_parts, lse_parts, *, dtype=None, out=None, lse=None):
     l = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=dev) if lse is None else lse
     _check_device_tensor("out", o, dev, dtype=dtype, shape=o_parts.shape[1:])
     _check_device_tensor("lse", l, dev, dtype=torch.float32, shape=lse_parts.shape[1:])
-    with torch.cuda.device(o_parts.device):
-        stream = torch.cuda.current_stream(o_parts.device).cuda_stream
-        rc = capi().flash_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, rows, D,
-                                     o.data_ptr(), l.data_ptr(), stream, _dtype_code(o))
-    _check(rc)
+    idx = o_parts.get_device()
+    code = _dtype_code(o)
+    _check(_on_device(idx, lambda: capi().flash_attn_merge(
+        o_parts.data_ptr(), lse_parts.data_ptr(), n, rows, D, o.data_ptr(), l.data_ptr(),
+        _stream_handle(idx), code)))
     return o, l
 
 
@@ -326,15 +366,14 @@ def flash_attn_bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int =
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     else:
         _check_workspace(workspace, q.device, need)
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = capi().flash_attn_bwd(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
-            int(bool(causal)), int(window), int(n_sink), float(scale),
-            None if alibi_slopes is None else alibi_slopes.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), stream, _dtype_code(q))
-    _check(rc)
+    idx = q.get_device()
+    code = _dtype_code(q)
+    _check(_on_device(idx, lambda: capi().flash_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
+        int(bool(causal)), int(window), int(n_sink), float(scale),
+        None if alibi_slopes is None else alibi_slopes.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(idx), code)))
     return dq, dk, dv
 
 
@@ -346,17 +385,15 @@ def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, *, causal: bool = False, windo
     dq, dk, dv to allocate nothing here either). Shapes whose state exceeds
     the scratch (B*H*S above about 4.19 million rows) raise NotImplementedError;
     calls that overlap in time on one GPU race on the scratch."""
-    import torch
     B, H, Hkv, S, D, scale, dq, dk, dv = _bwd_args(q, k, v, o, lse, dout, scale, alibi_slopes,
                                                    dq, dk, dv)
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = capi().flash_attn_bwd_noalloc(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
-            int(bool(causal)), int(window), int(n_sink), float(scale),
-            None if alibi_slopes is None else alibi_slopes.data_ptr(), stream, _dtype_code(q))
-    _check(rc)
+    idx = q.get_device()
+    code = _dtype_code(q)
+    _check(_on_device(idx, lambda: capi().flash_attn_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, S, D,
+        int(bool(causal)), int(window), int(n_sink), float(scale),
+        None if alibi_slopes is None else alibi_slopes.data_ptr(), _stream_handle(idx), code)))
     return dq, dk, dv
 
 
