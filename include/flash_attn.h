@@ -257,10 +257,14 @@ int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o,
  * flash_attn_tile_shape -- host-only query of the tile flash_attn_fwd uses for
  * a problem of this shape: *block_q query rows per work-group and *block_k keys
  * per streamed key/value block (the kernel and its work-group size are chosen
- * from B*H, S, D and dtype). Returns FA_OK, FA_ERR_INVALID (NULL output,
- * B/H/S < 1, unknown dtype) or FA_ERR_UNSUPPORTED (D not implemented).
- * Touches no GPU. The environment variable FLASH_ATTN_WAVES=4|8, if set,
- * overrides the work-group size of the bf16/f16 D=64/128 kernel (tuning aid).
+ * from B*H, S, D and dtype). With ALiBi slopes or a key split the bf16/f16
+ * D=64/128 kernel never takes the small-grid schedule, whose 64-row blocks
+ * (four key parts at D = 64) this query may report. Returns FA_OK,
+ * FA_ERR_INVALID (NULL output, B/H/S < 1, unknown dtype) or
+ * FA_ERR_UNSUPPORTED (D not implemented). Touches no GPU. Tuning aids, read
+ * per call when set: FLASH_ATTN_WAVES=4|8 fixes the work-group size of the
+ * bf16/f16 D=64/128 kernel, FLASH_ATTN_PARTS=0|2|4 the key parts of its
+ * small-grid schedule (0 = off).
  */
 int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,
                           int* block_k);

@@ -486,19 +486,37 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
 }
 
 // ------------------------------------------------------------------------ //
-// Key-halves schedule for grids too small to fill the chip (fewer than two
-// 4-wave work-groups per CU): 8 waves per work-group of 128 query rows, in
-// two halves of four. Wave w covers rows 32 (w & 3) .. +31 like the 4-wave
-// kernel, and half w >> 2 streams its own contiguous half of the query
-// block's key blocks through its own double-buffered K/V tiles, so every
-// SIMD holds two waves and each wave takes half the steps. At the end the
-// halves combine their (max, sum, O) row by row through LDS -- the same
-// rescale the online softmax applies between blocks -- and the first half
-// writes the result.
+// Small-grid schedule, for grids too small to fill the chip (fewer than two
+// 4-wave work-groups per CU): 8 waves per work-group, as KP key parts of
+// RW = 8 / KP waves. Wave w covers the 32 query rows 32 (w % RW) .. +31 of
+// the block of 32 RW rows, like the 4-wave kernel, and part w / RW streams
+// its own contiguous share of the block's key blocks through its own
+// double-buffered K/V tiles, so every SIMD holds two waves and each wave takes
+// 1/KP of the steps. KP = 2 keeps 128-row blocks; KP = 4 (D = 64) uses 64-row
+// blocks, twice the work-groups. At the end the parts combine their (max,
+// sum, O) row by row through LDS -- the rescale the online softmax applies
+// between blocks, part after part -- and the first part writes the result.
 // ------------------------------------------------------------------------ //
-template <typename T, int D>
-__device__ __forceinline__ void fwd_halves_body(const FwdParams& p, T* (&kbuf)[4], T* (&vbuf)[4]) {
-  constexpr int BR = 128;
+
+// Tile buffer BASE + idx for a run-time idx < CNT, as nested selects: an
+// indexed array of LDS pointers (or a long select chain, which the compiler
+// turns into one) would need a table of address-space casts, which the
+// backend cannot emit.
+template <int BASE, int CNT, typename T, int N>
+__device__ __forceinline__ T* pick_tile(T* (&buf)[N], int idx) {
+  static_assert(BASE + CNT <= N, "tile index range");
+  if constexpr (CNT == 1)
+    return buf[BASE];
+  else
+    return idx == 0 ? buf[BASE] : pick_tile<BASE + 1, CNT - 1>(buf, idx - 1);
+}
+
+template <typename T, int D, int KP>
+__device__ __forceinline__ void fwd_parts_body(const FwdParams& p, T* (&kbuf)[2 * KP],
+                                               T* (&vbuf)[2 * KP]) {
+  static_assert(KP == 2 || KP == 4, "two or four key parts");
+  constexpr int RW = 8 / KP;   // row waves per part
+  constexpr int BR = 32 * RW;
   constexpr int BC = kBCf;
   using C = Core<T, D, BR, 0>;
   static_assert(C::NT == 2, "four 16-key chunks per block");
@@ -506,8 +524,8 @@ __device__ __forceinline__ void fwd_halves_body(const FwdParams& p, T* (&kbuf)[4
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rw = wave & 3;      // row block of the wave
-  const int half = wave >> 2;   // key half of the wave
+  const int rw = wave % RW;     // row block of the wave
+  const int part = wave / RW;   // key part of the wave
 
   int qb, bh;
   wg_coords(p, wg_id(p), qb, bh);
@@ -521,26 +539,28 @@ __device__ __forceinline__ void fwd_halves_body(const FwdParams& p, T* (&kbuf)[4
 
   const BlockRange br = block_range<BR, BC>(q_lo, S, p.causal, p.window, p.n_sink);
   const int n_all = br.count();
-  const int n_first = (n_all + 1) / 2;   // the first half takes the odd block
-  const int steps = n_first;             // both halves run this many steps
+  // part k takes steps [bnd(k), bnd(k + 1)): the first parts take the extra
+  // blocks, so every part runs at most bnd(1) steps
+  auto bnd = [&](int k) __attribute__((always_inline)) { return (n_all * k + KP - 1) / KP; };
+  const int steps = bnd(1);
   if (p.block_pairs && tid == 0) atomicAdd(p.block_pairs, (unsigned long long)n_all);
 
   C core;
   core.init(p, Qh, q_lo + 32 * rw + (lane & 31), lane, bh);
 
-  // Half HALF: blocks [it_b, it_b + n_iter) of the query block, tiles in
-  // kbuf/vbuf[2 HALF + parity].
-  auto run = [&](auto half_c) __attribute__((always_inline)) {
-    constexpr int HALF = decltype(half_c)::value;
-    const int it_b = HALF ? n_first : 0;
-    const int n_iter = HALF ? n_all - n_first : n_first;
+  // Part PART: blocks [it_b, it_b + n_iter) of the query block, tiles in
+  // kbuf/vbuf[2 PART + parity].
+  auto run = [&](auto part_c) __attribute__((always_inline)) {
+    constexpr int PART = decltype(part_c)::value;
+    const int it_b = bnd(PART);
+    const int n_iter = bnd(PART + 1) - it_b;
     auto kb = [&](int t) __attribute__((always_inline)) { return br.kb(it_b + t); };
-    T* const k0s = kbuf[2 * HALF];
-    T* const k1s = kbuf[2 * HALF + 1];
-    T* const v0s = vbuf[2 * HALF];
-    T* const v1s = vbuf[2 * HALF + 1];
-    TileDma<T, D, 4, false> kdma;
-    TileDma<T, D, 4, true> vdma;
+    T* const k0s = kbuf[2 * PART];
+    T* const k1s = kbuf[2 * PART + 1];
+    T* const v0s = vbuf[2 * PART];
+    T* const v1s = vbuf[2 * PART + 1];
+    TileDma<T, D, RW, false> kdma;
+    TileDma<T, D, RW, true> vdma;
     kdma.init(rw, lane);
     vdma.init(rw, lane);
     if (n_iter > 0) {
@@ -593,55 +613,82 @@ __device__ __forceinline__ void fwd_halves_body(const FwdParams& p, T* (&kbuf)[4
     segment(std::true_type{}, 0, f0);
     segment(std::false_type{}, f0, f1);
     segment(std::true_type{}, f1, n_iter);
-    // a shorter half meets the longer one's barriers
+    // a shorter part meets the longer ones' barriers
     for (int it = n_iter; it < steps; ++it) __syncthreads();
+    // A later part stages its O, reference max and sum (see below).
+    if constexpr (PART > 0) {
+      float* const ostage = reinterpret_cast<float*>(pick_tile<(PART - 1) * RW, RW>(kbuf, rw));
+      float* const sstage = reinterpret_cast<float*>(vbuf[0]) + ((PART - 1) * RW + rw) * 3 * 64;
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ostage[(dt * 16 + r) * 64 + lane] = core.oacc[dt][r];
+      sstage[lane] = core.m_run;
+      sstage[64 + lane] = core.mc;
+      sstage[128 + lane] = core.l_run;
+    }
   };
-  if (half == 0)
-    run(std::integral_constant<int, 0>{});
-  else
-    run(std::integral_constant<int, 1>{});
-
-  // Combine the halves: the second half's O, reference max and sum go
-  // through LDS (the tile buffers are idle now), lane by lane: a lane of the
-  // partner wave holds the same rows and columns of O^T. Row block rw stages
-  // its O in K tile buffer rw and its three per-lane numbers in a slice of
-  // the first V tile buffer.
-  constexpr int NO = C::NDT * 16;   // O values per lane
-  static_assert(NO * 64 * sizeof(float) <= kBCf * D * sizeof(T), "one wave's O fits a tile");
-  static_assert(4 * 3 * 64 * sizeof(float) <= kBCf * D * sizeof(T), "the row numbers fit a tile");
-  T* const kst = rw == 0 ? kbuf[0] : rw == 1 ? kbuf[1] : rw == 2 ? kbuf[2] : kbuf[3];
-  float* const ostage = reinterpret_cast<float*>(kst);
-  float* const sstage = reinterpret_cast<float*>(vbuf[0]) + rw * 3 * 64;
-  if (half == 1) {
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ostage[(dt * 16 + r) * 64 + lane] = core.oacc[dt][r];
-    sstage[lane] = core.m_run;
-    sstage[64 + lane] = core.mc;
-    sstage[128 + lane] = core.l_run;
+  if constexpr (KP == 2) {
+    if (part == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  } else {
+    if (part == 0)
+      run(std::integral_constant<int, 0>{});
+    else if (part == 1)
+      run(std::integral_constant<int, 1>{});
+    else if (part == 2)
+      run(std::integral_constant<int, 2>{});
+    else
+      run(std::integral_constant<int, 3>{});
   }
+
+  // Combine the parts: each later part's O, reference max and sum went
+  // through LDS (the tile buffers are idle after the loop), lane by lane: a
+  // lane of a partner wave holds the same rows and columns of O^T. Part k > 0
+  // of row block rw staged its O in K tile buffer (k - 1) RW + rw and its
+  // three per-lane numbers in a slice of the first V tile buffer.
+  constexpr int NO = C::NDT * 16;   // O values per lane
+  constexpr int NST = (KP - 1) * RW;
+  static_assert(NST <= 2 * KP, "one K tile buffer per staged wave");
+  static_assert(NO * 64 * sizeof(float) <= kBCf * D * sizeof(T), "one wave's O fits a tile");
+  static_assert(NST * 3 * 64 * sizeof(float) <= kBCf * D * sizeof(T), "the row numbers fit a tile");
   __syncthreads();
-  if (half == 0) {
-    const float m1 = sstage[lane], mc1 = sstage[64 + lane], l1 = sstage[128 + lane];
-    const bool e0 = core.m_run == kNegInf, e1 = m1 == kNegInf;
-    const float m = e0 ? mc1 : (e1 ? core.mc : fmaxf(core.mc, mc1));
-    const float a0 = e0 ? 0.f : fast_exp2(core.mc - m);
-    const float a1 = e1 ? 0.f : fast_exp2(mc1 - m);
+  if (part == 0) {
+    auto fold = [&](auto k_c) __attribute__((always_inline)) {
+      constexpr int K = decltype(k_c)::value;
+      const float* const ostage =
+          reinterpret_cast<const float*>(pick_tile<(K - 1) * RW, RW>(kbuf, rw));
+      const float* const sstage =
+          reinterpret_cast<const float*>(vbuf[0]) + ((K - 1) * RW + rw) * 3 * 64;
+      const float m1 = sstage[lane], mc1 = sstage[64 + lane], l1 = sstage[128 + lane];
+      const bool e0 = core.m_run == kNegInf, e1 = m1 == kNegInf;
+      const float m = e0 ? mc1 : (e1 ? core.mc : fmaxf(core.mc, mc1));
+      const float a0 = e0 ? 0.f : fast_exp2(core.mc - m);
+      const float a1 = e1 ? 0.f : fast_exp2(mc1 - m);
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
+      for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        core.oacc[dt][r] = core.oacc[dt][r] * a0 + ostage[(dt * 16 + r) * 64 + lane] * a1;
-    core.l_run = core.l_run * a0 + l1 * a1;
-    core.mc = m;
+        for (int r = 0; r < 16; ++r)
+          core.oacc[dt][r] = core.oacc[dt][r] * a0 + ostage[(dt * 16 + r) * 64 + lane] * a1;
+      core.l_run = core.l_run * a0 + l1 * a1;
+      core.mc = m;
+      // (the folded state counts as having seen a key once either side did)
+      if (e0 && !e1) core.m_run = m1;
+    };
+    fold(std::integral_constant<int, 1>{});
+    if constexpr (KP == 4) {
+      fold(std::integral_constant<int, 2>{});
+      fold(std::integral_constant<int, 3>{});
+    }
     core.epilogue(p, head, bh);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int KP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fa_fwd_halves_kernel(FwdParams p) {
+void fa_fwd_parts_kernel(FwdParams p) {
   constexpr int TILE = kBCf * D;
   __shared__ __attribute__((aligned(1024))) T k0s[TILE];
   __shared__ __attribute__((aligned(1024))) T k1s[TILE];
@@ -651,9 +698,23 @@ void fa_fwd_halves_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) T v1s[TILE];
   __shared__ __attribute__((aligned(1024))) T v2s[TILE];
   __shared__ __attribute__((aligned(1024))) T v3s[TILE];
-  T* kbuf[4] = {k0s, k1s, k2s, k3s};
-  T* vbuf[4] = {v0s, v1s, v2s, v3s};
-  fwd_halves_body<T, D>(p, kbuf, vbuf);
+  if constexpr (KP == 4) {
+    __shared__ __attribute__((aligned(1024))) T k4s[TILE];
+    __shared__ __attribute__((aligned(1024))) T k5s[TILE];
+    __shared__ __attribute__((aligned(1024))) T k6s[TILE];
+    __shared__ __attribute__((aligned(1024))) T k7s[TILE];
+    __shared__ __attribute__((aligned(1024))) T v4s[TILE];
+    __shared__ __attribute__((aligned(1024))) T v5s[TILE];
+    __shared__ __attribute__((aligned(1024))) T v6s[TILE];
+    __shared__ __attribute__((aligned(1024))) T v7s[TILE];
+    T* kbuf[8] = {k0s, k1s, k2s, k3s, k4s, k5s, k6s, k7s};
+    T* vbuf[8] = {v0s, v1s, v2s, v3s, v4s, v5s, v6s, v7s};
+    fwd_parts_body<T, D, 4>(p, kbuf, vbuf);
+  } else {
+    T* kbuf[4] = {k0s, k1s, k2s, k3s};
+    T* vbuf[4] = {v0s, v1s, v2s, v3s};
+    fwd_parts_body<T, D, 2>(p, kbuf, vbuf);
+  }
 }
 
 template <typename T, int D, int NW, int AL>
@@ -700,19 +761,27 @@ FA_FAST_INST(_Float16, 128, 4)
 FA_FAST_INST(_Float16, 64, 8)
 FA_FAST_INST(_Float16, 64, 4)
 #undef FA_FAST_INST
-template __global__ void fa_fwd_halves_kernel<__bf16, 128>(FwdParams);
-template __global__ void fa_fwd_halves_kernel<__bf16, 64>(FwdParams);
-template __global__ void fa_fwd_halves_kernel<_Float16, 128>(FwdParams);
-template __global__ void fa_fwd_halves_kernel<_Float16, 64>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<__bf16, 128, 2>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<__bf16, 64, 2>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<__bf16, 64, 4>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<_Float16, 128, 2>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<_Float16, 64, 2>(FwdParams);
+template __global__ void fa_fwd_parts_kernel<_Float16, 64, 4>(FwdParams);
 
 
 
 template <typename T, int D, int AL>
 static void launch_fast_a(const FwdParams& p, int nw, hipStream_t st) {
   const unsigned grid = (unsigned)p.nqb * (unsigned)p.BH * (unsigned)p.n_split;
-  if (AL == 0 && p.halves) {
-    hipLaunchKernelGGL((fa_fwd_halves_kernel<T, D>), dim3(grid), dim3(512), 0, st, p);
+  if (AL == 0 && p.parts == 2) {
+    hipLaunchKernelGGL((fa_fwd_parts_kernel<T, D, 2>), dim3(grid), dim3(512), 0, st, p);
     return;
+  }
+  if constexpr (D == 64) {
+    if (AL == 0 && p.parts == 4) {
+      hipLaunchKernelGGL((fa_fwd_parts_kernel<T, D, 4>), dim3(grid), dim3(512), 0, st, p);
+      return;
+    }
   }
   if (nw == 8)
     hipLaunchKernelGGL((fa_fwd_fast_kernel<T, D, 8, AL>), dim3(grid), dim3(512), 0, st, p);

@@ -52,7 +52,7 @@ struct FwdParams {
   float c;      // |scale| * log2(e), at least FLT_MIN
   int neg;      // scale < 0
   int reverse;  // 1: work-groups take their tiles in reverse dispatch order (testing aid)
-  int halves;   // 1: the fast kernel's key-halves schedule (8 waves, small grids)
+  int parts;    // 2 or 4: the small-grid schedule with that many key parts (8 waves); 0: off
 };
 
 // Arguments of one backward launch (validated on the host). c = scale * log2(e)
@@ -84,7 +84,9 @@ struct Plan {
   int nw;        // waves per work-group of the fast kernel
   int block_q;   // query rows per work-group
   int block_k;   // keys per streamed block
+  int parts;     // key parts of the small-grid schedule (2 or 4), or 0
 };
-Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype);
+// plain: no ALiBi and no key split (the small-grid schedule needs both).
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain);
 
 }  // namespace fa

@@ -72,8 +72,18 @@ int reverse_order() {
 // least two 8-wave work-groups per CU) do 8 waves win, by halving the K/V
 // tile traffic per query row. FLASH_ATTN_WAVES=4|8 overrides the wave count
 // (tuning only).
-Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype) {
+//
+// Grids of fewer than two 4-wave work-groups of 128 rows per CU (256 CUs)
+// leave SIMDs with one wave or none. Without ALiBi and a key split they take
+// the small-grid schedule: 8-wave work-groups whose waves split each query
+// block's key blocks into key parts, so that every SIMD holds two waves and
+// each wave takes 1/parts of the steps. Two parts keep 128-row blocks; four
+// parts (D = 64, where the tiles of four parts fit in LDS) use 64-row blocks,
+// which doubles the work-group count of a grid that covers at most half the
+// CUs. FLASH_ATTN_PARTS=0|2|4 overrides (tuning).
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain) {
   Plan pl;
+  pl.parts = 0;
   if (fast_supported(D, dtype)) {
     pl.fast = true;
     // 8-wave work-groups (256 rows) for S >= 16384 when there are at least 512
@@ -88,6 +98,16 @@ Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype) {
     }
     pl.block_q = 32 * pl.nw;
     pl.block_k = kFastBC;
+    if (plain && pl.nw == 4) {
+      const int64_t nb = S / 128 + (S % 128 != 0);
+      if (BH < 512 && nb < 512 && BH * nb < 512) pl.parts = (D == 64 && BH * nb <= 128) ? 4 : 2;
+      if (const char* e = std::getenv("FLASH_ATTN_PARTS")) {
+        if (e[0] == '0') pl.parts = 0;
+        if (e[0] == '2') pl.parts = 2;
+        if (e[0] == '4') pl.parts = D == 64 ? 4 : 2;
+      }
+      if (pl.parts == 4) pl.block_q = 64;
+    }
   } else {
     pl.fast = false;
     pl.nw = 4;
@@ -161,7 +181,7 @@ int prepare_fwd(const FwdCall& a, FwdLaunch* out, std::string* err) {
   if (n_split > 1 && !fast_supported(D, a.dtype))
     return fail(err, FA_ERR_UNSUPPORTED,
                 "key splitting needs bf16 / f16 with head dim 64 or 128");
-  const Plan plan = plan_fwd(bh, S, D, a.dtype);
+  const Plan plan = plan_fwd(bh, S, D, a.dtype, !a.alibi && n_split == 1);
   const int64_t br = plan.block_q;
   const int64_t nqb = (S + br - 1) / br;
   // grid = nqb * bh * n_split work-groups (times 256 threads at most) in 32 bits;
@@ -205,14 +225,7 @@ int prepare_fwd(const FwdCall& a, FwdLaunch* out, std::string* err) {
   p.c = cf;
   p.neg = a.scale < 0.f ? 1 : 0;
   p.reverse = reverse_order();
-  // Grids of fewer than two 4-wave work-groups per CU (256 CUs) take the
-  // key-halves schedule (no ALiBi, no key split): two waves on every SIMD,
-  // each with half the key blocks. FLASH_ATTN_HALVES=0|1 overrides (tuning).
-  p.halves = plan.fast && plan.nw == 4 && !a.alibi && n_split == 1 && nqb * bh < 512;
-  if (const char* e = std::getenv("FLASH_ATTN_HALVES")) {
-    if (e[0] == '0') p.halves = 0;
-    if (e[0] == '1') p.halves = plan.fast && plan.nw == 4 && !a.alibi && n_split == 1;
-  }
+  p.parts = plan.parts;
   out->plan = plan;
   out->rows = rows;
   return FA_OK;
@@ -380,7 +393,7 @@ int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block
   if (elem_bytes(dtype) == 0) return fail(err, FA_ERR_INVALID, "unknown dtype");
   if (!supported_d(D)) return fail(err, FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
   if (B > INT64_MAX / H) return fail(err, FA_ERR_INVALID, "B*H overflows");
-  const Plan plan = plan_fwd(B * H, S, D, dtype);
+  const Plan plan = plan_fwd(B * H, S, D, dtype, true);
   *block_q = plan.block_q;
   *block_k = plan.block_k;
   return FA_OK;

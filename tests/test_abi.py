@@ -63,6 +63,29 @@ def test_version_and_tile_shape():
         fa.flash_attn_tile_shape(1, 1, 64, 64, 7)
 
 
+def test_small_grid_tile_choice(monkeypatch):
+    """The plan behind flash_attn_tile_shape: a D = 64 grid of at most 128
+    work-groups of 128 rows (half the CUs) takes four key parts on 64-row
+    blocks; other grids of fewer than 512 keep 128-row blocks (two parts, or
+    8 waves at S >= 16384); FLASH_ATTN_PARTS=0|2|4 overrides."""
+    monkeypatch.delenv("FLASH_ATTN_PARTS", raising=False)
+    monkeypatch.delenv("FLASH_ATTN_WAVES", raising=False)
+    for dt in (fa.FA_F16, fa.FA_BF16):
+        assert fa.flash_attn_tile_shape(2, 8, 1024, 64, dt) == (64, 64)       # 128 work-groups
+        assert fa.flash_attn_tile_shape(1, 1, 1, 64, dt) == (64, 64)
+        assert fa.flash_attn_tile_shape(1, 16, 2048, 64, dt) == (128, 64)    # 256: two parts
+        assert fa.flash_attn_tile_shape(1, 32, 2048, 64, dt) == (128, 64)    # 512: 4 waves
+        assert fa.flash_attn_tile_shape(2, 8, 1024, 128, dt) == (128, 64)    # D = 128: two parts
+        assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt) == (128, 64)
+        assert fa.flash_attn_tile_shape(1, 32, 16384, 128, dt) == (256, 64)  # 8 waves
+    monkeypatch.setenv("FLASH_ATTN_PARTS", "0")
+    assert fa.flash_attn_tile_shape(2, 8, 1024, 64, fa.FA_F16) == (128, 64)
+    monkeypatch.setenv("FLASH_ATTN_PARTS", "4")
+    assert fa.flash_attn_tile_shape(1, 32, 2048, 64, fa.FA_F16) == (64, 64)
+    assert fa.flash_attn_tile_shape(2, 8, 1024, 128, fa.FA_F16) == (128, 64)
+    assert fa.flash_attn_tile_shape(1, 1, 1024, 64, fa.FA_F32)[0] == 128   # generic kernel
+
+
 def _call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, S=64, D=64, causal=0, window=0, n_sink=0,
           scale=0.125, stream=None, dtype=fa.FA_BF16, counter=None):
     c = fa.capi()

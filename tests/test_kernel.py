@@ -462,18 +462,20 @@ def test_grid_order_reversal_bitwise():
         assert torch.equal(ref[0], rev[0]) and torch.equal(ref[1], rev[1]), c
 
 
-@pytest.mark.parametrize("halves", ["0", "1"])
-@pytest.mark.parametrize("dtype, D", [("bf16", 128), ("f16", 64)])
-def test_both_small_grid_schedules(halves, dtype, D):
-    """Grids of fewer than 512 work-groups take the key-halves schedule by
-    default (no ALiBi, no key split); FLASH_ATTN_HALVES=0|1, read per call,
-    forces either schedule. Both against the oracle: the 4-wave kernel keeps
-    its small-size coverage, and the key-halves kernel meets a half with no
-    visible key (one key block, a narrow window), an odd block count and
-    ragged tails. Sink counts 32 and 33 straddle the 4-wave kernel's
-    half-width sink step (taken when every sink lies in the first 32 keys of
-    the sink block)."""
-    os.environ["FLASH_ATTN_HALVES"] = halves
+@pytest.mark.parametrize("parts, dtype, D", [("0", "bf16", 128), ("2", "bf16", 128),
+                                             ("0", "f16", 64), ("2", "f16", 64), ("4", "f16", 64),
+                                             ("4", "bf16", 64)])
+def test_every_small_grid_schedule(parts, dtype, D):
+    """Grids of fewer than 512 work-groups of 128 rows take the small-grid
+    schedule by default (no ALiBi, no key split): two key parts, or four on
+    64-row blocks at D = 64 when the grid covers at most half the CUs.
+    FLASH_ATTN_PARTS=0|2|4, read per call, forces a schedule. Each against
+    the oracle: the 4-wave kernel keeps its small-size coverage, and the
+    key-part kernels meet parts with no visible key (one key block, a narrow
+    window), uneven block counts and ragged tails. Sink counts 32 and 33
+    straddle the 4-wave kernel's half-width sink step (taken when every sink
+    lies in the first 32 keys of the sink block)."""
+    os.environ["FLASH_ATTN_PARTS"] = parts
     try:
         for S in (1, 64, 65, 129, 700, 1000):
             q, k, v = fa_inputs.make_qkv(1, 2, S, D, dtype, seed=S + 11 * D)
@@ -482,9 +484,9 @@ def test_both_small_grid_schedules(halves, dtype, D):
                 o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
                 compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
                         n_sink=n_sink,
-                        label=f"halves={halves} {dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
+                        label=f"parts={parts} {dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
     finally:
-        del os.environ["FLASH_ATTN_HALVES"]
+        del os.environ["FLASH_ATTN_PARTS"]
 
 
 # --------------------------------------------------------------------------- #
@@ -501,11 +503,11 @@ def _pairs_with_visible_keys(S, bq, bk, causal, window, n_sink):
     return total
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("S,causal,window,n_sink", [
     (64, True, 0, 0), (4096, True, 0, 0), (4096, False, 0, 0), (1000, True, 0, 0),
     (8192, True, 1024, 4), (3000, True, 200, 70), (3000, True, 200, 0)])
-def test_block_pairs_visited(S, causal, window, n_sink):
-    D = 128
+def test_block_pairs_visited(S, causal, window, n_sink, D):
     bq, bk = fa.flash_attn_tile_shape(1, 1, S, D, fa.FA_BF16)
     q, k, v = fa_inputs.make_qkv(1, 1, S, D, "bf16", seed=1)
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
