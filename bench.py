@@ -110,14 +110,12 @@ def copy_probe(mib: int, steps: int):
 
 
 def kernel_name(fa, w) -> str:
-    if w.backward:
-        return (f"fa::fa_bwd_dq_kernel + fa::fa_bwd_dkv_kernel <{w.dtype},D={w.D}> "
-                "(128-row / 128-key tiles)")
     code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w.dtype]
-    bq, bk = fa.flash_attn_tile_shape(w.B, w.H, w.S, w.D, code)
-    if w.dtype != "f32" and w.D in (64, 128):
-        return f"fa::fa_fwd_fast_kernel<{w.dtype},D={w.D},waves={bq // 32}> ({bq}x{bk} tile)"
-    return f"fa::fa_fwd_{'f32' if w.dtype == 'f32' else 'half'}_kernel<D={w.D}> ({bq}x{bk} tile)"
+    if w.backward:
+        return "fa::" + fa.flash_attn_bwd_kernel(w.B, w.H, w.S, w.D, code, H_kv=w.kv_heads,
+                                                 causal=w.causal, window=w.window, alibi=w.alibi)
+    return "fa::" + fa.flash_attn_fwd_kernel(w.B, w.H, w.S, w.D, code, alibi=w.alibi,
+                                             n_split=w.n_split)
 
 
 def nominal_flops(w) -> float:

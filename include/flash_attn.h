@@ -270,6 +270,34 @@ int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
                           int* block_k);
 
 /*
+ * flash_attn_fwd_kernel -- host-only query of the kernel a forward call would
+ * launch for this problem: writes a NUL-terminated description (kernel
+ * template, dtype, head dim, work-group shape, tile) into the caller's host
+ * buffer buf of buf_bytes bytes, truncated to fit (128 bytes always suffice).
+ * alibi: nonzero when slopes are passed (flash_attn_fwd_ext); n_split: 1, or
+ * the key split of flash_attn_fwd_split. Returns FA_OK, FA_ERR_INVALID (NULL
+ * or empty buffer, B/H/S < 1, unknown dtype, n_split outside [1, 256]; buf
+ * then holds "") or FA_ERR_UNSUPPORTED (head dim, or a split the fast kernel
+ * cannot take). Touches no GPU; honours FLASH_ATTN_WAVES and
+ * FLASH_ATTN_PARTS like the calls.
+ */
+int flash_attn_fwd_kernel(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
+                          int64_t n_split, char* buf, int64_t buf_bytes);
+
+/*
+ * flash_attn_bwd_kernel -- host-only query of the two kernels flash_attn_bwd
+ * (and flash_attn_bwd_noalloc) would launch: the dQ kernel, then one of two
+ * dK/dV kernels, chosen from the grid, the causal mask, the window and ALiBi.
+ * Writes a NUL-terminated description into buf (buf_bytes bytes, truncated
+ * to fit; 256 bytes always suffice). Returns FA_OK, FA_ERR_INVALID (NULL or
+ * empty buffer, B/H/S < 1, H_kv not dividing H, unknown dtype, window < 0;
+ * buf then holds "") or FA_ERR_UNSUPPORTED (not bf16 / f16 with D 64 or
+ * 128). Touches no GPU; honours FLASH_ATTN_DKV=1|2 like the call.
+ */
+int flash_attn_bwd_kernel(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int dtype,
+                          int causal, int64_t window, int alibi, char* buf, int64_t buf_bytes);
+
+/*
  * flash_attn_last_error -- text of the last error raised on the calling
  * thread (empty string if none). The pointer stays valid until the thread's
  * next call into this library.

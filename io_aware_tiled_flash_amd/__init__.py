@@ -15,7 +15,8 @@ import os
 __all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_noalloc", "flash_attn_fwd_counted",
            "flash_attn_fwd_split",
            "flash_attn_merge", "flash_attn_bwd_workspace_bytes",
-           "flash_attn_split_workspace_bytes", "flash_attn_tile_shape",
+           "flash_attn_split_workspace_bytes", "flash_attn_tile_shape", "flash_attn_fwd_kernel",
+           "flash_attn_bwd_kernel",
            "flash_attn_last_error", "flash_attn_version", "capi", "library_path",
            "FA_F32", "FA_F16", "FA_BF16", "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED",
            "FA_ERR_HIP"]
@@ -63,6 +64,11 @@ class _CAPI:
         self.flash_attn_tile_shape = self._fn(
             "flash_attn_tile_shape",
             [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
+        self.flash_attn_fwd_kernel = self._fn(
+            "flash_attn_fwd_kernel", [i64, i64, i64, i64, i32, i32, i64, ctypes.c_char_p, i64], i32)
+        self.flash_attn_bwd_kernel = self._fn(
+            "flash_attn_bwd_kernel",
+            [i64, i64, i64, i64, i64, i32, i32, i64, i32, ctypes.c_char_p, i64], i32)
         self.flash_attn_last_error = self._fn("flash_attn_last_error", [], ctypes.c_char_p)
         self.flash_attn_version = self._fn("flash_attn_version", [], ctypes.c_char_p)
 
@@ -99,6 +105,23 @@ def flash_attn_tile_shape(B: int, H: int, S: int, D: int, dtype: int) -> tuple[i
     rc = capi().flash_attn_tile_shape(B, H, S, D, dtype, ctypes.byref(bq), ctypes.byref(bk))
     _check(rc)
     return bq.value, bk.value
+
+
+def flash_attn_fwd_kernel(B: int, H: int, S: int, D: int, dtype: int, *, alibi: bool = False,
+                          n_split: int = 1) -> str:
+    """Description of the kernel a forward call would launch for this problem."""
+    buf = ctypes.create_string_buffer(128)
+    _check(capi().flash_attn_fwd_kernel(B, H, S, D, dtype, int(bool(alibi)), n_split, buf, 128))
+    return buf.value.decode()
+
+
+def flash_attn_bwd_kernel(B: int, H: int, S: int, D: int, dtype: int, *, H_kv: int | None = None,
+                          causal: bool = False, window: int = 0, alibi: bool = False) -> str:
+    """Description of the kernels a backward call would launch for this problem."""
+    buf = ctypes.create_string_buffer(256)
+    _check(capi().flash_attn_bwd_kernel(B, H, H if H_kv is None else H_kv, S, D, dtype,
+                                        int(bool(causal)), window, int(bool(alibi)), buf, 256))
+    return buf.value.decode()
 
 
 def _check(rc: int):

@@ -3,7 +3,9 @@
 // contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <string>
 
 #include "../../include/flash_attn.h"
@@ -203,6 +205,37 @@ int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
                           int* block_k) {
   g_last_error.clear();
   return fa::tile_shape(B, H, S, D, dtype, block_q, block_k, &g_last_error);
+}
+
+int flash_attn_fwd_kernel(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
+                          int64_t n_split, char* buf, int64_t buf_bytes) {
+  g_last_error.clear();
+  if (!buf || buf_bytes < 1) {
+    g_last_error = "null or empty output buffer";
+    return FA_ERR_INVALID;
+  }
+  std::string name;
+  const int rc = fa::fwd_kernel_name(B, H, S, D, dtype, alibi, n_split, &name, &g_last_error);
+  const size_t n = rc == FA_OK ? std::min(name.size(), (size_t)(buf_bytes - 1)) : 0;
+  std::memcpy(buf, name.data(), n);
+  buf[n] = '\0';
+  return rc;
+}
+
+int flash_attn_bwd_kernel(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int dtype,
+                          int causal, int64_t window, int alibi, char* buf, int64_t buf_bytes) {
+  g_last_error.clear();
+  if (!buf || buf_bytes < 1) {
+    g_last_error = "null or empty output buffer";
+    return FA_ERR_INVALID;
+  }
+  std::string name;
+  const int rc =
+      fa::bwd_kernel_name(B, H, H_kv, S, D, dtype, causal, window, alibi, &name, &g_last_error);
+  const size_t n = rc == FA_OK ? std::min(name.size(), (size_t)(buf_bytes - 1)) : 0;
+  std::memcpy(buf, name.data(), n);
+  buf[n] = '\0';
+  return rc;
 }
 
 const char* flash_attn_last_error(void) { return g_last_error.c_str(); }

@@ -176,6 +176,92 @@ __device__ __forceinline__ void rows_to_lds(float* lds, const float* g, int lane
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
 
+// RowOffsets in two registers: the chunk index 2 s + h and the row swizzle
+// share no bits above bit 0 of the swizzle, so (2 s + h) ^ sw = ((2 s) ^ sh)
+// + (h ^ (sw & 1)) with sh = sw & ~1, and off(s) = base + ((16 s) ^ (sh << 3))
+// costs one XOR with a constant per k-step instead of a register per k-step.
+template <int D>
+struct RowOffsets2 {
+  int base, sh8;
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, col = lane & 31;
+    const int sw = k_swz<D>(col);
+    base = col * D + ((h ^ (sw & 1)) << 3);
+    sh8 = (sw & ~1) << 3;
+  }
+  __device__ __forceinline__ int off(int s) const { return base + ((16 * s) ^ sh8); }
+};
+
+// TrOffsets in four registers, by the same split: the chunk index 4 dt + c
+// (c < 4) and the swizzle share no bits above bit 1, so lo / hi (dt) =
+// base + ((32 dt) ^ (swizzle & ~3) << 3) for the row of either half.
+template <int D>
+struct TrOffsets2 {
+  int base[2], sh8[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, grp = (lane >> 4) & 1, r16 = lane & 15;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      const int row = 4 * h + (r16 >> 2) + 8 * part;
+      const int sw = k_swz<D>(row);
+      const int c = 2 * grp + ((r16 & 3) >> 1);
+      base[part] = row * D + ((c ^ (sw & 3)) << 3) + 4 * (r16 & 1);
+      sh8[part] = (sw & ~3) << 3;
+    }
+  }
+  __device__ __forceinline__ int lo(int dt) const { return base[0] + ((32 * dt) ^ sh8[0]); }
+  __device__ __forceinline__ int hi(int dt) const { return base[1] + ((32 * dt) ^ sh8[1]); }
+};
+
+// Direct-to-LDS copy of ROWS rows of D elements (K layout: 16-byte chunks
+// XOR-swizzled by row, as TileDma) by NW waves. Rows past the sequence end
+// read as zeros (the descriptor ends there).
+template <typename T, int D, int ROWS, int NW>
+struct RowsDma {
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int NI = ROWS * CPR / (64 * NW);   // instructions per wave
+  static_assert(NI >= 1 && NI * 64 * NW == ROWS * CPR, "tile / wave split");
+  uint32_t voff[NI];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int pos = (wave * NI + n) * 64 + lane;
+      const int row = pos / CPR;
+      const int pc = pos % CPR;
+      voff[n] = (uint32_t)((row * D + 8 * (pc ^ k_swz<D>(row))) * (int)sizeof(T));
+    }
+  }
+
+  // rows [r0, r0 + ROWS) of g (r0 < S) into lds
+  __device__ __forceinline__ void load(T* lds, const T* __restrict__ g, int r0, int S,
+                                       int wave) const {
+    const uint64_t g64 = reinterpret_cast<uint64_t>(g);
+    const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g64);
+    const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g64 >> 32));
+    const uint64_t base = (((uint64_t)ghi << 32) | glo) + (uint64_t)(uint32_t)r0 * (D * sizeof(T));
+    const int bytes = min(S - r0, ROWS) * D * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(base), (short)0, bytes, kBufferFlags);
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (wave * NI + n) * 512), 16,
+                                               voff[n], 0, 0, 0);
+  }
+};
+
+// Direct-to-LDS copy of 32 consecutive fp32 values from g to lds[0..31],
+// issued by one wave (lanes 32..63 fall outside the descriptor and read 0
+// into lds[32..63]).
+__device__ __forceinline__ void rows32_to_lds(float* lds, const float* g, int lane) {
+  const uint64_t g64 = reinterpret_cast<uint64_t>(g);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)g64);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(g64 >> 32));
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, 32 * 4, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, (uint32_t)lane * 4u, 0, 0, 0);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------ //
@@ -613,11 +699,251 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------ //
+// dkv kernel, two independent work-groups per CU
+// ------------------------------------------------------------------------ //
+// 4 waves x 32 keys per work-group. K of a wave's keys stays in registers
+// (the B operand of S), V of the block is staged once in LDS and 32-row Q /
+// dO tiles are double-buffered: about 65 KiB of LDS, so two work-groups share
+// a CU and each SIMD holds one wave of each, out of step with each other.
+template <typename T, int D, bool ALIBI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkv2_kernel(BwdParams p) {
+  constexpr int BK = 128;   // keys per work-group: 4 waves of 32
+  constexpr int BQ = 32;    // query rows per streamed block
+  constexpr int NS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int KT = BK * D;
+  constexpr int QT = BQ * D;
+  using Tr = Half16<T>;
+  using v8 = typename Tr::v8;
+
+  __shared__ __attribute__((aligned(1024))) T vs[KT];
+  // two stages of Q and dO: the stage being read and the stage being loaded
+  // are distinct objects, so the compiler needs no wait on the loads in
+  // flight before its LDS reads
+  __shared__ __attribute__((aligned(1024))) T q0s[QT];
+  __shared__ __attribute__((aligned(1024))) T q1s[QT];
+  __shared__ __attribute__((aligned(1024))) T d0s[QT];
+  __shared__ __attribute__((aligned(1024))) T d1s[QT];
+  // [lse * log2(e) (64) | delta (64)] per stage (32 rows used of each)
+  __shared__ __attribute__((aligned(16))) float r0s[128];
+  __shared__ __attribute__((aligned(16))) float r1s[128];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int BHkv = p.BH / p.G;
+  const int bkv = (int)blockIdx.x % BHkv;
+  const int kb = (int)blockIdx.x / BHkv;
+  const int S = p.S;
+  const int k_lo = kb * BK;
+  const int j = k_lo + 32 * wave + col;   // this lane's key
+  const size_t kv_head = (size_t)bkv * S * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
+  const T* __restrict__ Vh = uniform_ptr(reinterpret_cast<const T*>(p.v) + kv_head);
+
+  RowOffsets2<D> ro;
+  ro.init(lane);
+  TrOffsets2<D> tro;
+  tro.init(lane);
+  RowsDma<T, D, BK, 4> vdma;
+  vdma.init(wave, lane);
+  RowsDma<T, D, BQ, 4> qdma;
+  qdma.init(wave, lane);
+
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+  v8 kf[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) kf[s2] = load_frag<T>(Kh, j, S, D, 16 * s2 + 8 * h);
+
+  int qfirst, qlast;
+  query_range(p, k_lo, min(k_lo + BK, S) - 1, BQ, qfirst, qlast);
+  // mask of a partially visible pair for row i = q0 + 4 h + e (e = 8 g + r4)
+  // and this lane's key j: keep iff i >= j and (i - j < window or j < n_sink)
+  const int big = 1 << 30;
+  const bool sinkj = p.window > 0 && j < p.n_sink;
+  const int wlen = p.window > 0 ? p.window : big;
+
+  // steps: (query head gi, query block) in order, n_q blocks per head
+  const int n_q = qlast - qfirst + 1;
+  const int n_iter = n_q > 0 ? p.G * n_q : 0;
+  auto tile_src = [&](int it, int& bh, int& q0) __attribute__((always_inline)) {
+    const int gi = it / n_q;
+    bh = bkv * p.G + gi;   // query head (b * H + h)
+    q0 = (qfirst + it - gi * n_q) * BQ;
+  };
+  // the Q / dO tiles and the lse2 / delta rows of step `it` into one stage
+  auto tile_load = [&](T* qd, T* dd, float* rd, int it) __attribute__((always_inline)) {
+    int bh, q0;
+    tile_src(it, bh, q0);
+    const size_t head = (size_t)bh * S * D;
+    qdma.load(qd, reinterpret_cast<const T*>(p.q) + head, q0, S, wave);
+    qdma.load(dd, reinterpret_cast<const T*>(p.dout) + head, q0, S, wave);
+    if (wave == 0) {
+      const size_t rb = (size_t)bh * p.Sp + q0;
+      rows32_to_lds(rd, p.lse2 + rb, lane);
+      rows32_to_lds(rd + 64, p.delta + rb, lane);
+    }
+  };
+  vdma.load(vs, Vh, k_lo, S, wave);
+  if (n_iter > 0) tile_load(q0s, d0s, r0s, 0);
+  wait_vmem<0>();
+  __syncthreads();
+
+  const T* const kw_v = vs + 32 * wave * D;
+  auto block_full_kv = [&](int q0) __attribute__((always_inline)) {
+    bool full = true;
+    if (p.causal) {
+      full = q0 >= k_lo + BK - 1;
+      if (p.window > 0)
+        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
+    }
+    return full;
+  };
+  auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr bool MASK = decltype(mask)::value;
+    const T* qs = PAR == 0 ? q0s : q1s;
+    const T* dos = PAR == 0 ? d0s : d1s;
+    const float* rs = PAR == 0 ? r0s : r1s;
+    int bh, q0;
+    tile_src(it, bh, q0);
+    if (it + 1 < n_iter) {
+      if (PAR == 0)
+        tile_load(q1s, d1s, r1s, it + 1);
+      else
+        tile_load(q0s, d0s, r0s, it + 1);
+    }
+    const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
+    const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
+    const int ewin = emin + wlen;
+    // The LDS offsets pass through an empty asm each step, so the read
+    // addresses are formed here (one add each) instead of being hoisted out
+    // of the loop, where 30-odd of them do not fit the register budget.
+    RowOffsets2<D> rl = ro;
+    TrOffsets2<D> tl = tro;
+    asm volatile("" : "+v"(rl.base), "+v"(rl.sh8), "+v"(tl.base[0]), "+v"(tl.base[1]),
+                 "+v"(tl.sh8[0]), "+v"(tl.sh8[1]));
+    f32x16 sc, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = 0.f;
+      dp[r] = 0.f;
+    }
+    // S = Q K^T (K in registers) and dP = dO V^T (dO, V from LDS), reads
+    // pinned two k-steps ahead of their MFMAs: left free, the scheduler
+    // hoists every read and the kernel spills; the other work-group's wave on
+    // the SIMD covers the read latency.
+    v8 qa[2], da[2], va[2];
+    qa[0] = lds_row8(qs + rl.off(0));
+    qa[1] = lds_row8(qs + rl.off(1));
+    da[0] = lds_row8(dos + rl.off(0));
+    va[0] = lds_row8(kw_v + rl.off(0));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) {
+        da[(s + 1) & 1] = lds_row8(dos + rl.off(s + 1));
+        va[(s + 1) & 1] = lds_row8(kw_v + rl.off(s + 1));
+      }
+      sc = Tr::mma(qa[s & 1], kf[s], sc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 2 < NS) qa[s & 1] = lds_row8(qs + rl.off(s + 2));
+      dp = Tr::mma(da[s & 1], va[s & 1], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // this lane's rows of the block: 8 g + 4 h + (0..3)
+    f32x4 l2[4], dd[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l2[g] = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * h);
+      dd[g] = *reinterpret_cast<const f32x4*>(rs + 64 + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int g = r >> 2, e4 = r & 3;
+      const int e = 8 * g + e4;
+      float x;
+      if (ALIBI)
+        x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
+      else
+        x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
+      float pr = fast_exp2(x);
+      if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
+      sc[r] = pr;                        // P
+      dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
+    }
+    // P and dS as MFMA B operands (16 rows each half); the fp32 tiles die here
+    const v8 pb[2] = {pack8<T>(sc, 0), pack8<T>(sc, 1)};
+    const v8 db[2] = {pack8<T>(dp, 0), pack8<T>(dp, 1)};
+    __builtin_amdgcn_sched_barrier(0);
+    // dV^T += dO^T P and dK^T += Q^T dS: per (16-row half u, 32-wide d tile)
+    // the two transposed operands, one pair ahead of its MFMAs
+    auto tr_reads = [&](int u, int dt, v8& o, v8& q) __attribute__((always_inline)) {
+      const T* qq = qs + 16 * u * D;
+      const T* oo = dos + 16 * u * D;
+      o = lds_tr8(oo + tl.lo(dt), oo + tl.hi(dt));
+      q = lds_tr8(qq + tl.lo(dt), qq + tl.hi(dt));
+    };
+    v8 oT, qT;
+    tr_reads(0, 0, oT, qT);
+#pragma unroll
+    for (int x = 0; x < 2 * NDT; ++x) {
+      const int u = x / NDT, dt = x % NDT;
+      v8 on = oT, qn = qT;
+      if (x + 1 < 2 * NDT) tr_reads((x + 1) / NDT, (x + 1) % NDT, on, qn);
+      dv[dt] = Tr::mma(oT, pb[u], dv[dt]);
+      dk[dt] = Tr::mma(qT, db[u], dk[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+      oT = on;
+      qT = qn;
+    }
+    wait_vmem<0>();
+    __syncthreads();
+  };
+  auto segment = [&](auto mask, int b, int e) __attribute__((always_inline)) {
+    int it = b;
+    if (it < e && (it & 1)) step(std::integral_constant<int, 1>{}, mask, it++);
+    for (; it + 2 <= e; it += 2) {
+      step(std::integral_constant<int, 0>{}, mask, it);
+      step(std::integral_constant<int, 1>{}, mask, it + 1);
+    }
+    if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
+  };
+  // Per query head [partially visible][fully visible][partially visible]
+  // query blocks (the causal diagonal first, the window's end last).
+  if (n_q > 0) {
+    int f0 = 0;
+    while (f0 < n_q && !block_full_kv((qfirst + f0) * BQ)) ++f0;
+    int f1 = f0;
+    while (f1 < n_q && block_full_kv((qfirst + f1) * BQ)) ++f1;
+    for (int gi = 0; gi < p.G; ++gi) {
+      const int b = gi * n_q;
+      segment(std::true_type{}, b, b + f0);
+      segment(std::false_type{}, b + f0, b + f1);
+      segment(std::true_type{}, b + f1, b + n_q);
+    }
+  }
+  if (j < S) {
+    store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
+    store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);
+  }
+}
+
 #define FA_BWD_INST(T, D)                                                \
   template __global__ void fa_bwd_dq_kernel<T, D, false>(BwdParams);     \
   template __global__ void fa_bwd_dq_kernel<T, D, true>(BwdParams);      \
   template __global__ void fa_bwd_dkv_kernel<T, D, false>(BwdParams);    \
-  template __global__ void fa_bwd_dkv_kernel<T, D, true>(BwdParams);
+  template __global__ void fa_bwd_dkv_kernel<T, D, true>(BwdParams);     \
+  template __global__ void fa_bwd_dkv2_kernel<T, D, false>(BwdParams);   \
+  template __global__ void fa_bwd_dkv2_kernel<T, D, true>(BwdParams);
 FA_BWD_INST(__bf16, 128)
 FA_BWD_INST(__bf16, 64)
 FA_BWD_INST(_Float16, 128)
@@ -664,7 +990,12 @@ static hipError_t launch_bwd_a(const BwdParams& p, hipStream_t st) {
   const unsigned g1 = (unsigned)p.nqb * (unsigned)p.BH;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, ALIBI>), dim3(g1), dim3(64 * kBwdWaves), 0, st, p);
   const unsigned g2 = (unsigned)p.nkb * (unsigned)(p.BH / p.G);
-  hipLaunchKernelGGL((fa_bwd_dkv_kernel<T, D, ALIBI>), dim3(g2), dim3(64 * kBwdWaves), 0, st, p);
+  // dK/dV: two 4-wave work-groups per CU, or one 4-wave work-group per CU
+  // (the host's choice, bwd_dkv_pair)
+  if (p.dkv_pair)
+    hipLaunchKernelGGL((fa_bwd_dkv2_kernel<T, D, ALIBI>), dim3(g2), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((fa_bwd_dkv_kernel<T, D, ALIBI>), dim3(g2), dim3(64 * kBwdWaves), 0, st, p);
   return hipGetLastError();
 }
 

@@ -378,7 +378,41 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   p.n_sink = (p.window == 0) ? 0 : (int)(a.n_sink < S ? a.n_sink : S);
   p.scale = a.scale;
   p.c = (float)((double)a.scale * 1.4426950408889634);
+  p.dkv_pair = bwd_dkv_pair(nb * (B * H_kv), a.causal != 0, p.window > 0, a.alibi != nullptr);
   return FA_OK;
+}
+
+int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int dtype, int causal,
+                    int64_t window, int alibi, std::string* name, std::string* err) {
+  if (!name) return fail(err, FA_ERR_INVALID, "null output pointer");
+  if (B < 1 || H < 1 || S < 1) return fail(err, FA_ERR_INVALID, "B, H and S must be >= 1");
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(err, FA_ERR_INVALID, "key/value heads must be >= 1 and divide the query heads");
+  if (elem_bytes(dtype) == 0) return fail(err, FA_ERR_INVALID, "unknown dtype");
+  if (window < 0) return fail(err, FA_ERR_INVALID, "window must be >= 0");
+  if (!bwd_supported(D, dtype))
+    return fail(err, FA_ERR_UNSUPPORTED,
+                "the backward pass needs bf16 / f16 with head dim 64 or 128");
+  if (B > INT64_MAX / H) return fail(err, FA_ERR_INVALID, "B*H overflows");
+  const int64_t nb = S / kBwdRows + (S % kBwdRows != 0);
+  const int64_t kv = B * H_kv;
+  const int64_t grid = kv > INT64_MAX / nb ? INT64_MAX : nb * kv;
+  const bool pair = bwd_dkv_pair(grid, causal != 0, window > 0 && window < S, alibi != 0);
+  const std::string t = std::string("<") + (dtype == kDtypeF16 ? "f16" : "bf16") + ",D=" +
+                        std::to_string(D) + ">";
+  *name = "fa_bwd_dq_kernel" + t + " (128 rows, 4 waves) + " +
+          (pair ? "fa_bwd_dkv2_kernel" + t + " (128 keys, 4 waves, 2 work-groups per CU)"
+                : "fa_bwd_dkv_kernel" + t + " (128 keys, 4 waves, 1 work-group per CU)");
+  return FA_OK;
+}
+
+bool bwd_dkv_pair(int64_t grid, bool causal, bool window, bool alibi) {
+  bool pair = !alibi && !window && (grid >= 1024 || (!causal && grid >= 512));
+  if (const char* e = std::getenv("FLASH_ATTN_DKV")) {
+    if (e[0] == '1') pair = false;
+    if (e[0] == '2') pair = true;
+  }
+  return pair;
 }
 
 void bwd_bind_workspace(BwdParams* p, void* ws) {
@@ -396,6 +430,34 @@ int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block
   const Plan plan = plan_fwd(B * H, S, D, dtype, true);
   *block_q = plan.block_q;
   *block_k = plan.block_k;
+  return FA_OK;
+}
+
+int fwd_kernel_name(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
+                    int64_t n_split, std::string* name, std::string* err) {
+  if (!name) return fail(err, FA_ERR_INVALID, "null output pointer");
+  if (B < 1 || H < 1 || S < 1) return fail(err, FA_ERR_INVALID, "B, H and S must be >= 1");
+  const int e = elem_bytes(dtype);
+  if (e == 0) return fail(err, FA_ERR_INVALID, "unknown dtype");
+  if (n_split < 1 || n_split > 256) return fail(err, FA_ERR_INVALID, "n_split must be in [1, 256]");
+  if (!supported_d(D)) return fail(err, FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+  if (n_split > 1 && !fast_supported(D, dtype))
+    return fail(err, FA_ERR_UNSUPPORTED, "key splitting needs bf16 / f16 with head dim 64 or 128");
+  if (B > INT64_MAX / H) return fail(err, FA_ERR_INVALID, "B*H overflows");
+  const Plan plan = plan_fwd(B * H, S, D, dtype, !alibi && n_split == 1);
+  const char* ty = dtype == kDtypeF32 ? "f32" : dtype == kDtypeF16 ? "f16" : "bf16";
+  const std::string d = std::to_string(D);
+  const std::string tile = " (" + std::to_string(plan.block_q) + "x" + std::to_string(plan.block_k) + " tile)";
+  if (!plan.fast)
+    *name = std::string(dtype == kDtypeF32 ? "fa_fwd_f32_kernel<D=" : "fa_fwd_half_kernel<D=") + d +
+            ">" + tile;
+  else if (plan.parts)
+    *name = std::string("fa_fwd_parts_kernel<") + ty + ",D=" + d + ",parts=" +
+            std::to_string(plan.parts) + "> (8 waves, " + tile.substr(2);
+  else
+    *name = std::string("fa_fwd_fast_kernel<") + ty + ",D=" + d + ",waves=" +
+            std::to_string(plan.nw) + (alibi ? ",alibi" : "") + ">" + tile;
+  if (n_split > 1) *name += " + fa_merge_kernel";
   return FA_OK;
 }
 

@@ -88,4 +88,12 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, std::string* err);
 int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q, int* block_k,
                std::string* err);
 
+// flash_attn_bwd_kernel: writes the kernels' description to *name.
+int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int dtype, int causal,
+                    int64_t window, int alibi, std::string* name, std::string* err);
+
+// flash_attn_fwd_kernel: writes the kernel's description to *name.
+int fwd_kernel_name(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
+                    int64_t n_split, std::string* name, std::string* err);
+
 }  // namespace fa

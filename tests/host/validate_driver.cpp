@@ -397,6 +397,12 @@ int main() {
     int bq, bk;
     (void)fa::tile_shape(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4), &bq,
                          &bk, &err);
+    std::string kname;
+    (void)fa::fwd_kernel_name(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4),
+                              (int)(rng.next() % 2), rng.size(), &kname, &err);
+    (void)fa::bwd_kernel_name(rng.size(), rng.size(), rng.size(), rng.size(), rng.size(),
+                              (int)(rng.next() % 4), (int)(rng.next() % 2), rng.size(),
+                              (int)(rng.next() % 2), &kname, &err);
   }
   std::printf("fuzz: %d forward and %d backward calls accepted of 200000 each\n", ok_fwd, ok_bwd);
   if (g_failures) {

@@ -78,8 +78,27 @@ def test_small_grid_tile_choice(monkeypatch):
         assert fa.flash_attn_tile_shape(2, 8, 1024, 128, dt) == (128, 64)    # D = 128: two parts
         assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt) == (128, 64)
         assert fa.flash_attn_tile_shape(1, 32, 16384, 128, dt) == (256, 64)  # 8 waves
+    c2 = fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16)
+    assert c2 == "fa_fwd_parts_kernel<f16,D=64,parts=4> (8 waves, 64x64 tile)", c2
+    assert "parts=2" in fa.flash_attn_fwd_kernel(2, 8, 1024, 128, fa.FA_BF16)
+    assert "waves=4" in fa.flash_attn_fwd_kernel(4, 16, 4096, 128, fa.FA_BF16)
+    assert "waves=8" in fa.flash_attn_fwd_kernel(1, 32, 16384, 128, fa.FA_BF16)
+    # ALiBi and key splits never take the small-grid schedule
+    assert "fast_kernel" in fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, alibi=True)
+    assert fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, n_split=4).endswith("fa_merge_kernel")
+    assert fa.flash_attn_fwd_kernel(1, 1, 64, 16, fa.FA_F32).startswith("fa_fwd_f32_kernel<D=16>")
+    with pytest.raises(NotImplementedError):
+        fa.flash_attn_fwd_kernel(1, 1, 64, 48, fa.FA_BF16)
+    with pytest.raises(NotImplementedError):
+        fa.flash_attn_fwd_kernel(1, 1, 64, 32, fa.FA_BF16, n_split=2)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd_kernel(1, 1, 64, 64, fa.FA_BF16, n_split=0)
+    buf = ctypes.create_string_buffer(8)   # truncated to fit, NUL-terminated
+    assert fa.capi().flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, 0, 1, buf, 8) == fa.FA_OK
+    assert buf.value == b"fa_fwd_"
     monkeypatch.setenv("FLASH_ATTN_PARTS", "0")
     assert fa.flash_attn_tile_shape(2, 8, 1024, 64, fa.FA_F16) == (128, 64)
+    assert "waves=4" in fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16)
     monkeypatch.setenv("FLASH_ATTN_PARTS", "4")
     assert fa.flash_attn_tile_shape(1, 32, 2048, 64, fa.FA_F16) == (64, 64)
     assert fa.flash_attn_tile_shape(2, 8, 1024, 128, fa.FA_F16) == (128, 64)
@@ -373,3 +392,30 @@ def test_bwd_noalloc_unsupported_types():
     for kw in (dict(dtype=fa.FA_F32), dict(D=32)):
         rc, msg = _call_bwd_noalloc(**kw)
         assert rc == fa.FA_ERR_UNSUPPORTED, (kw, msg)
+
+
+def test_backward_kernel_choice(monkeypatch):
+    """The dK/dV kernel of a backward: two 4-wave work-groups per CU on grids
+    of at least 1024 work-groups of 128 keys (512 without the causal mask),
+    with neither ALiBi nor a window; else one per CU. FLASH_ATTN_DKV=1|2
+    overrides."""
+    monkeypatch.delenv("FLASH_ATTN_DKV", raising=False)
+    bk = fa.flash_attn_bwd_kernel
+    head = bk(4, 16, 4096, 128, fa.FA_BF16, causal=True)
+    assert head.startswith("fa_bwd_dq_kernel<bf16,D=128>") and "fa_bwd_dkv2_kernel" in head, head
+    assert "dkv2" in bk(2, 16, 2048, 128, fa.FA_BF16, causal=False)          # 512, no mask
+    assert "dkv2" not in bk(1, 16, 4096, 128, fa.FA_BF16, causal=True)       # 512, causal
+    assert "dkv2" not in bk(4, 16, 4096, 128, fa.FA_BF16, H_kv=2, causal=True)   # 256
+    assert "dkv2" not in bk(4, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)
+    assert "dkv2" not in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=1024)
+    assert "dkv2" in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=8192)   # no-op window
+    monkeypatch.setenv("FLASH_ATTN_DKV", "2")
+    assert "dkv2" in bk(1, 1, 64, 64, fa.FA_F16, causal=True)
+    monkeypatch.setenv("FLASH_ATTN_DKV", "1")
+    assert "dkv2" not in bk(4, 16, 4096, 128, fa.FA_BF16, causal=True)
+    with pytest.raises(NotImplementedError):
+        bk(1, 1, 64, 32, fa.FA_BF16)
+    with pytest.raises(NotImplementedError):
+        bk(1, 1, 64, 64, fa.FA_F32)
+    with pytest.raises(ValueError):
+        bk(1, 3, 64, 64, fa.FA_BF16, H_kv=2)

@@ -786,6 +786,18 @@ def _grad_err(got, ref):
                  max(1.0, float(np.abs(ref).max())))
 
 
+@pytest.fixture(params=["1", "2"])
+def dkv_kernel(request):
+    """Runs a backward test with each dK/dV kernel (FLASH_ATTN_DKV=1: one
+    wave per SIMD, K/V in registers; 2: two waves per SIMD, K/V in LDS),
+    read per call."""
+    os.environ["FLASH_ATTN_DKV"] = request.param
+    try:
+        yield request.param
+    finally:
+        del os.environ["FLASH_ATTN_DKV"]
+
+
 def _bwd_case(B, H, Hkv, S, D, dtype, causal, window, n_sink, scale, seed, slopes=None,
               heads=None, label=""):
     q, _, _ = fa_inputs.make_qkv(B, H, S, D, dtype, seed=seed)
@@ -811,14 +823,14 @@ def _bwd_case(B, H, Hkv, S, D, dtype, causal, window, n_sink, scale, seed, slope
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_backward(dtype, D):
+def test_backward(dtype, D, dkv_kernel):
     for S in (1, 63, 200, 333):
         for causal, window, n_sink in MASKS:
             _bwd_case(1, 2, 2, S, D, dtype, causal, window, n_sink, 1.0 / math.sqrt(D),
                       seed=S + D, label=f"{dtype} D{D} S{S} c{int(causal)} w{window} s{n_sink}")
 
 
-def test_backward_random_configurations():
+def test_backward_random_configurations(dkv_kernel):
     """A seeded sweep of the backward over batch, grouped heads, ragged S, D,
     dtype, mask, ALiBi and the scale's sign, each against the oracle's
     gradients."""
@@ -889,7 +901,7 @@ def test_backward_sequence_longer_than_2_to_the_24():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_backward_grouped_heads_alibi_scale(dtype):
+def test_backward_grouped_heads_alibi_scale(dtype, dkv_kernel):
     """Grouped K/V heads (dk, dv sum over the group), ALiBi, negative and zero
     scale."""
     _bwd_case(2, 4, 2, 257, 128, dtype, True, 0, 0, 0.088, seed=3, label="gqa")
@@ -904,7 +916,7 @@ def test_backward_grouped_heads_alibi_scale(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_backward_sharp_softmax(dtype):
+def test_backward_sharp_softmax(dtype, dkv_kernel):
     """Q x 6: nearly one-hot probability rows, so P is recomputed from scores far
     from the row max (exp2 arguments down to about -100) and dS is dominated by
     a few keys per row."""
@@ -936,7 +948,7 @@ def test_split_keys_sharp_softmax():
                 label=f"bf16 Qx8 split{n_split}")
 
 
-def test_backward_headline_shape_sampled():
+def test_backward_headline_shape_sampled(dkv_kernel):
     """The headline shape (B4 H16 S4096 D128 bf16 causal): two heads against
     the oracle, the rest finite."""
     B, H, S, D = 4, 16, 4096, 128
