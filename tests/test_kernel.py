@@ -853,7 +853,7 @@ def test_backward_random_configurations(dkv_kernel):
                         f"s{n_sink} scale {scale:+.3f} alibi {slopes is not None}")
 
 
-def test_backward_sequence_longer_than_2_to_the_24():
+def test_backward_sequence_longer_than_2_to_the_24(dkv_kernel):
     """The backward on one head of S = 2^24 + 77 keys (4.3 GB per tensor) with a
     64-key window, checked on sampled rows against the oracle run on compact
     copies: dQ of row i needs only keys [i - W + 1, i]; dK and dV of key j need
