@@ -437,12 +437,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
     }
     if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
   };
-  int f0 = 0;
-  while (f0 < n_iter && !block_full<BR, BC>(q_lo, br.kb(f0) * BC, S, p.causal, p.window, p.n_sink))
-    ++f0;
-  int f1 = f0;
-  while (f1 < n_iter && block_full<BR, BC>(q_lo, br.kb(f1) * BC, S, p.causal, p.window, p.n_sink))
-    ++f1;
+  const StepRange fr = local_steps(
+      full_key_steps(q_lo, BR, BC, S, p.causal, p.window, br.n_sinkb, br.kb_lo, br.kb_hi), 0,
+      n_iter, false);
+  const int f0 = fr.lo, f1 = fr.hi;
   segment(std::true_type{}, 0, f0);
   segment(std::false_type{}, f0, f1);
   segment(std::true_type{}, f1, n_iter);
@@ -539,15 +537,6 @@ void fa_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < BQ / kBCf; ++u)
       dma.load(dst + u * kBCf * D, src, min(q0 + u * kBCf, S - 1), S, wave);
-  };
-  auto block_full_kv = [&](int q0) __attribute__((always_inline)) {
-    bool full = true;
-    if (p.causal) {
-      full = q0 >= k_lo + BK - 1;
-      if (p.window > 0)
-        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
-    }
-    return full;
   };
   // rows [q0, q0 + BQ) of the padded per-row arrays (no bounds checks: q0 +
   // BQ <= Sp) into dst = [lse * log2(e) | delta]
@@ -682,10 +671,9 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   // code and no branch: a branch per step would make the compiler copy the
   // dK / dV accumulators at every join.
   if (n_q > 0) {
-    int f0 = 0;
-    while (f0 < n_q && !block_full_kv((qfirst + f0) * BQ)) ++f0;
-    int f1 = f0;
-    while (f1 < n_q && block_full_kv((qfirst + f1) * BQ)) ++f1;
+    const StepRange fr = local_steps(
+        full_query_steps(k_lo, BK, BQ, p.causal, p.window, p.n_sink, qfirst, qlast), 0, n_q, false);
+    const int f0 = fr.lo, f1 = fr.hi;
     for (int gi = 0; gi < p.G; ++gi) {
       const int b = gi * n_q;
       segment(std::true_type{}, b, b + f0);
@@ -799,15 +787,6 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
   __syncthreads();
 
   const T* const kw_v = vs + 32 * wave * D;
-  auto block_full_kv = [&](int q0) __attribute__((always_inline)) {
-    bool full = true;
-    if (p.causal) {
-      full = q0 >= k_lo + BK - 1;
-      if (p.window > 0)
-        full = full && ((q0 + BQ - 1 - k_lo < p.window) || (k_lo + BK <= p.n_sink));
-    }
-    return full;
-  };
   auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     constexpr bool MASK = decltype(mask)::value;
@@ -920,10 +899,9 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
   // Per query head [partially visible][fully visible][partially visible]
   // query blocks (the causal diagonal first, the window's end last).
   if (n_q > 0) {
-    int f0 = 0;
-    while (f0 < n_q && !block_full_kv((qfirst + f0) * BQ)) ++f0;
-    int f1 = f0;
-    while (f1 < n_q && block_full_kv((qfirst + f1) * BQ)) ++f1;
+    const StepRange fr = local_steps(
+        full_query_steps(k_lo, BK, BQ, p.causal, p.window, p.n_sink, qfirst, qlast), 0, n_q, false);
+    const int f0 = fr.lo, f1 = fr.hi;
     for (int gi = 0; gi < p.G; ++gi) {
       const int b = gi * n_q;
       segment(std::true_type{}, b, b + f0);

@@ -460,12 +460,12 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
     }
     if (it < e) step(std::integral_constant<int, 0>{}, mask, it, Full{});
   };
-  int f0 = 0;
-  while (f0 < n_iter && !block_full<BR, BC>(q_lo, kb(f0) * BC, S, p.causal, p.window, p.n_sink))
-    ++f0;
-  int f1 = f0;
-  while (f1 < n_iter && block_full<BR, BC>(q_lo, kb(f1) * BC, S, p.causal, p.window, p.n_sink))
-    ++f1;
+  // the fully visible run, in closed form (a scan over the blocks here cost
+  // about 4 us per work-group)
+  const StepRange fr = local_steps(
+      full_key_steps(q_lo, BR, BC, S, p.causal, p.window, br.n_sinkb, br.kb_lo, br.kb_hi), it_b,
+      n_iter, AL == 1);
+  const int f0 = fr.lo, f1 = fr.hi;
   // A walk that starts with the sink block (a window whose first block lies
   // past it) sees in that block only the keys below n_sink; with at most 32
   // sinks its second sub-tile is hidden, so that step computes half a block.
@@ -604,12 +604,10 @@ __device__ __forceinline__ void fwd_parts_body(const FwdParams& p, T* (&kbuf)[2 
       }
       if (it < e) step(std::integral_constant<int, 0>{}, mask, it);
     };
-    int f0 = 0;
-    while (f0 < n_iter && !block_full<BR, BC>(q_lo, kb(f0) * BC, S, p.causal, p.window, p.n_sink))
-      ++f0;
-    int f1 = f0;
-    while (f1 < n_iter && block_full<BR, BC>(q_lo, kb(f1) * BC, S, p.causal, p.window, p.n_sink))
-      ++f1;
+    const StepRange fr = local_steps(
+        full_key_steps(q_lo, BR, BC, S, p.causal, p.window, br.n_sinkb, br.kb_lo, br.kb_hi), it_b,
+        n_iter, false);
+    const int f0 = fr.lo, f1 = fr.hi;
     segment(std::true_type{}, 0, f0);
     segment(std::false_type{}, f0, f1);
     segment(std::true_type{}, f1, n_iter);

@@ -21,6 +21,68 @@ constexpr int kBwdRows = 128;
 // fp32 per-row arrays of 4M rows (B*H*S with S rounded up to kBwdRows).
 constexpr int64_t kBwdScratchBytes = (int64_t)32 << 20;
 
+// ---- Mask segments of a block walk (constexpr: usable in kernels and on the host) ----
+//
+// The kernels walk their blocks in three segments: [partially visible][fully
+// visible][partially visible], where only the end segments carry mask code.
+// The functions below give the fully visible run in closed form. Any run of
+// fully visible blocks is correct to use (the masked step is exact on a fully
+// visible block too); these return the run the mask geometry makes contiguous.
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// a / b rounded towards -inf / +inf, for b > 0 and any sign of a
+constexpr int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+constexpr int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
+
+struct StepRange {
+  int lo, hi;   // steps [lo, hi)
+};
+
+// Forward (and dQ): query rows [q_lo, q_lo + BR), key blocks of BC keys; the
+// walk visits n_sinkb sink blocks, then key blocks kb_lo .. kb_hi. Key block
+// kb is fully visible when its keys end at or before the sequence end, and
+// under the causal mask at or before the first row, and with a window start
+// inside the last row's window (q_lo + BR - 1 - kb BC < window). Those bound
+// one run [ka, kz] of the window's blocks. (A block fully visible only because
+// all its keys are sinks is left to a masked segment.) Returns the walk steps
+// of that run.
+constexpr StepRange full_key_steps(int q_lo, int BR, int BC, int S, int causal, int window,
+                                   int n_sinkb, int kb_lo, int kb_hi) {
+  int ka = kb_lo, kz = cmin(kb_hi, S / BC - 1);
+  if (causal) {
+    kz = cmin(kz, (q_lo + 1) / BC - 1);
+    if (window > 0) ka = cmax(ka, ceil_div(q_lo + BR - window, BC));
+  }
+  if (ka > kz) return StepRange{n_sinkb, n_sinkb};
+  return StepRange{n_sinkb + ka - kb_lo, n_sinkb + kz - kb_lo + 1};
+}
+
+// dK/dV: keys [k_lo, k_lo + BK), query blocks of BQ rows qfirst .. qlast. Query
+// block qb is fully visible when (causal) its first row is at or after the
+// last key and (window) its last row is within the window of the first key,
+// or every key is a sink. Returns the run as query-block offsets from qfirst.
+constexpr StepRange full_query_steps(int k_lo, int BK, int BQ, int causal, int window, int n_sink,
+                                     int qfirst, int qlast) {
+  int qa = qfirst, qz = qlast;
+  if (causal) {
+    qa = cmax(qa, ceil_div(k_lo + BK - 1, BQ));
+    if (window > 0 && k_lo + BK > n_sink) qz = cmin(qz, floor_div(k_lo + window - BQ, BQ));
+  }
+  if (qa > qz) return StepRange{0, 0};
+  return StepRange{qa - qfirst, qz - qfirst + 1};
+}
+
+// The steps of F as positions in a walk over steps [it_b, it_b + n), taken in
+// reverse order when rev (position t visits step it_b + n - 1 - t).
+constexpr StepRange local_steps(StepRange F, int it_b, int n, bool rev) {
+  int lo = rev ? it_b + n - F.hi : F.lo - it_b;
+  int hi = rev ? it_b + n - F.lo : F.hi - it_b;
+  lo = cmin(cmax(lo, 0), n);
+  hi = cmin(cmax(hi, lo), n);
+  return StepRange{lo, hi};
+}
+
 inline bool fast_supported(int64_t D, int dtype) {
   return (dtype == kDtypeBF16 || dtype == kDtypeF16) && (D == 64 || D == 128);
 }

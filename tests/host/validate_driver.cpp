@@ -5,6 +5,7 @@
 // random extreme arguments (sizes near the int64 limits, addresses near the
 // top of the address space) through every entry so the sanitizers see any
 // overflow or out-of-bounds access. No GPU and no HIP runtime is involved.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -306,6 +307,106 @@ int main() {
     expect(fa::tile_shape(1, 1, 64, 48, FA_BF16, &bq, &bk, &err) == FA_ERR_UNSUPPORTED, "tile d48");
     expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, &bq, &bk, &err) == FA_OK && bk == fa::kFastBC,
            "tile c3");
+  }
+
+  // ---- closed-form mask segments against a scan of the blocks ----
+  // The kernels take their fully visible run of blocks from full_key_steps /
+  // full_query_steps. Every step of that run must be fully visible, and
+  // without sink keys it must be exactly the first fully visible run (what a
+  // scan of the walk finds). The walk and the visibility test restate the mask
+  // geometry: sink blocks first, then the window's blocks (forward, dQ); the
+  // query blocks that see a key block (dK/dV).
+  {
+    Rng g{777};
+    int checked = 0, exact = 0;
+    for (int trial = 0; trial < 200000; ++trial) {
+      const int BC = 64;
+      const int BR = (int[]){64, 128, 256}[g.next() % 3];
+      const int S = 1 + (int)(g.next() % 3000);
+      const int causal = (int)(g.next() % 4 != 0);
+      const int window = causal && (g.next() % 2) ? 1 + (int)(g.next() % 600) : 0;
+      const int n_sink = window ? (int)(g.next() % 200) : 0;
+      const int q_lo = BR * (int)(g.next() % ((S + BR - 1) / BR));
+      // the walk
+      int n_sinkb = 0, kb_lo = 0, kb_hi;
+      if (causal) {
+        kb_hi = (std::min(q_lo + BR, S) - 1) / BC;
+        if (window > 0) {
+          kb_lo = std::max(0, q_lo - window + 1) / BC;
+          n_sinkb = std::min(kb_lo, (n_sink + BC - 1) / BC);
+        }
+      } else {
+        kb_hi = (S - 1) / BC;
+      }
+      const int n_all = n_sinkb + kb_hi - kb_lo + 1;
+      auto kb_of = [&](int it) { return it < n_sinkb ? it : kb_lo + it - n_sinkb; };
+      auto full = [&](int kb) {
+        const int k0 = kb * BC;
+        bool f = k0 + BC <= S;
+        if (causal) {
+          f = f && k0 + BC - 1 <= q_lo;
+          if (window > 0) f = f && (q_lo + BR - 1 - k0 < window || k0 + BC <= n_sink);
+        }
+        return f;
+      };
+      // a sub-walk (a key split's share), forwards or in reverse
+      const int it_b = (int)(g.next() % n_all);
+      const int n = 1 + (int)(g.next() % (n_all - it_b));
+      const bool rev = g.next() % 2;
+      const fa::StepRange F = fa::full_key_steps(q_lo, BR, BC, S, causal, window, n_sinkb, kb_lo, kb_hi);
+      const fa::StepRange r = fa::local_steps(F, it_b, n, rev);
+      auto step_kb = [&](int t) { return kb_of(rev ? it_b + n - 1 - t : it_b + t); };
+      bool ok = 0 <= r.lo && r.lo <= r.hi && r.hi <= n;
+      for (int t = r.lo; ok && t < r.hi; ++t) ok = full(step_kb(t));
+      expect(ok, "full_key_steps: a step of the run is not fully visible (S " + std::to_string(S) +
+                     ", q_lo " + std::to_string(q_lo) + ", window " + std::to_string(window) + ")");
+      if (n_sink == 0) {
+        int f0 = 0;
+        while (f0 < n && !full(step_kb(f0))) ++f0;
+        int f1 = f0;
+        while (f1 < n && full(step_kb(f1))) ++f1;
+        const bool same = f1 == f0 ? r.lo == r.hi : (r.lo == f0 && r.hi == f1);
+        expect(same, "full_key_steps: not the scanned run (S " + std::to_string(S) + ", q_lo " +
+                         std::to_string(q_lo) + ", BR " + std::to_string(BR) + ", window " +
+                         std::to_string(window) + ", rev " + std::to_string(rev) + ")");
+        ++exact;
+      }
+      ++checked;
+      // dK/dV: key block [k_lo, k_lo + BK), query blocks of BQ rows
+      const int BK = 128, BQ = (g.next() % 2) ? 32 : 128;
+      const int k_lo = BK * (int)(g.next() % ((S + BK - 1) / BK));
+      const int k_hi = std::min(k_lo + BK, S) - 1;
+      const int nqb = (S + BQ - 1) / BQ;
+      int qfirst = 0, qlast = nqb - 1;
+      if (causal) {
+        qfirst = k_lo / BQ;
+        if (window > 0 && k_lo >= n_sink) qlast = std::min(S - 1, k_hi + window - 1) / BQ;
+      }
+      if (qfirst > qlast) continue;
+      const int nq = qlast - qfirst + 1;
+      auto qfull = [&](int qb) {
+        const int q0 = qb * BQ;
+        bool f = true;
+        if (causal) {
+          f = q0 >= k_lo + BK - 1;
+          if (window > 0) f = f && (q0 + BQ - 1 - k_lo < window || k_lo + BK <= n_sink);
+        }
+        return f;
+      };
+      const fa::StepRange rq = fa::local_steps(
+          fa::full_query_steps(k_lo, BK, BQ, causal, window, n_sink, qfirst, qlast), 0, nq, false);
+      bool okq = 0 <= rq.lo && rq.lo <= rq.hi && rq.hi <= nq;
+      for (int t = rq.lo; okq && t < rq.hi; ++t) okq = qfull(qfirst + t);
+      int q0 = 0;
+      while (q0 < nq && !qfull(qfirst + q0)) ++q0;
+      int q1 = q0;
+      while (q1 < nq && qfull(qfirst + q1)) ++q1;
+      const bool sameq = q1 == q0 ? rq.lo == rq.hi : (rq.lo == q0 && rq.hi == q1);
+      expect(okq && sameq, "full_query_steps (S " + std::to_string(S) + ", k_lo " +
+                               std::to_string(k_lo) + ", BQ " + std::to_string(BQ) + ", window " +
+                               std::to_string(window) + ", sinks " + std::to_string(n_sink) + ")");
+    }
+    std::printf("mask segments: %d walks checked, %d against the scanned run\n", checked, exact);
   }
 
   // ---- fuzz: random extreme arguments through every entry ----
