@@ -287,7 +287,8 @@ int flash_attn_fwd_kernel(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
 /*
  * flash_attn_bwd_kernel -- host-only query of the two kernels flash_attn_bwd
  * (and flash_attn_bwd_noalloc) would launch: the dQ kernel, then one of two
- * dK/dV kernels, chosen from the grid, the causal mask, the window and ALiBi.
+ * dK/dV kernels, chosen from the grid, the causal mask and the window; alibi
+ * (nonzero when slopes are passed) selects the ALiBi instances of both.
  * Writes a NUL-terminated description into buf (buf_bytes bytes, truncated
  * to fit; 256 bytes always suffice). Returns FA_OK, FA_ERR_INVALID (NULL or
  * empty buffer, B/H/S < 1, H_kv not dividing H, unknown dtype, window < 0;

@@ -818,46 +818,70 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
       dp[r] = 0.f;
     }
     // S = Q K^T (K in registers) and dP = dO V^T (dO, V from LDS), reads
-    // pinned two k-steps ahead of their MFMAs: left free, the scheduler
-    // hoists every read and the kernel spills; the other work-group's wave on
-    // the SIMD covers the read latency.
-    v8 qa[2], da[2], va[2];
-    qa[0] = lds_row8(qs + rl.off(0));
-    qa[1] = lds_row8(qs + rl.off(1));
-    da[0] = lds_row8(dos + rl.off(0));
-    va[0] = lds_row8(kw_v + rl.off(0));
+    // pinned two k-steps ahead of their MFMAs (one with ALiBi, whose bias
+    // terms need the registers): left free, the scheduler hoists every read
+    // and the kernel spills; the other work-group's wave on the SIMD covers
+    // the read latency.
+    if constexpr (!ALIBI) {
+      v8 qa[2], da[2], va[2];
+      qa[0] = lds_row8(qs + rl.off(0));
+      qa[1] = lds_row8(qs + rl.off(1));
+      da[0] = lds_row8(dos + rl.off(0));
+      va[0] = lds_row8(kw_v + rl.off(0));
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s + 1 < NS) {
-        da[(s + 1) & 1] = lds_row8(dos + rl.off(s + 1));
-        va[(s + 1) & 1] = lds_row8(kw_v + rl.off(s + 1));
+      for (int s = 0; s < NS; ++s) {
+        if (s + 1 < NS) {
+          da[(s + 1) & 1] = lds_row8(dos + rl.off(s + 1));
+          va[(s + 1) & 1] = lds_row8(kw_v + rl.off(s + 1));
+        }
+        sc = Tr::mma(qa[s & 1], kf[s], sc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 2 < NS) qa[s & 1] = lds_row8(qs + rl.off(s + 2));
+        dp = Tr::mma(da[s & 1], va[s & 1], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sc = Tr::mma(qa[s & 1], kf[s], sc);
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + 2 < NS) qa[s & 1] = lds_row8(qs + rl.off(s + 2));
-      dp = Tr::mma(da[s & 1], va[s & 1], dp);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // this lane's rows of the block: 8 g + 4 h + (0..3)
-    f32x4 l2[4], dd[4];
+    } else {
+      v8 qa = lds_row8(qs + rl.off(0));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+      for (int s = 0; s < NS; ++s) {
+        const v8 da = lds_row8(dos + rl.off(s)), va = lds_row8(kw_v + rl.off(s));
+        sc = Tr::mma(qa, kf[s], sc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < NS) qa = lds_row8(qs + rl.off(s + 1));
+        dp = Tr::mma(da, va, dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // this lane's rows of the block: 8 g + 4 h + (0..3); with ALiBi their
+    // lse2 / delta are read one group of four at a time, pinned (all 32 at
+    // once ran that build out of registers)
+    f32x4 l2[4], dd[4];
+    const auto read_rows = [&](int g) {
       l2[g] = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * h);
       dd[g] = *reinterpret_cast<const f32x4*>(rs + 64 + 8 * g + 4 * h);
+    };
+    if constexpr (!ALIBI) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) read_rows(g);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int g = r >> 2, e4 = r & 3;
-      const int e = 8 * g + e4;
-      float x;
-      if (ALIBI)
-        x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
-      else
-        x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
-      float pr = fast_exp2(x);
-      if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
-      sc[r] = pr;                        // P
-      dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (ALIBI) read_rows(g);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int r = 4 * g + e4;
+        const int e = 8 * g + e4;
+        float x;
+        if (ALIBI)
+          x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
+        else
+          x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
+        float pr = fast_exp2(x);
+        if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
+        sc[r] = pr;                        // P
+        dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
+      }
+      if constexpr (ALIBI) __builtin_amdgcn_sched_barrier(0);
     }
     // P and dS as MFMA B operands (16 rows each half); the fp32 tiles die here
     const v8 pb[2] = {pack8<T>(sc, 0), pack8<T>(sc, 1)};

@@ -144,11 +144,11 @@ struct BwdParams {
 // registers, V in LDS, 32-row query tiles) when the grid fills the chip
 // well, else one work-group per CU with K and V in registers. Measured on
 // gfx950: the pair wins by 5-11 % on grids of 1024 work-groups and more
-// without ALiBi or a window, and by 5 % on a 512-work-group grid without the
-// causal mask; it loses where ALiBi makes it spill, under a window, on a
-// single causal round of 512 work-groups (imbalance) and on smaller grids.
+// without a window (ALiBi included), and by 5 % on a 512-work-group grid
+// without the causal mask; it loses under a window, on a single causal round
+// of 512 work-groups (imbalance) and on smaller grids.
 // FLASH_ATTN_DKV=1|2 forces one (tuning, tests).
-bool bwd_dkv_pair(int64_t grid, bool causal, bool window, bool alibi);
+bool bwd_dkv_pair(int64_t grid, bool causal, bool window);
 
 // Which kernel and tile a problem runs with (a pure function of the shape and
 // of the FLASH_ATTN_WAVES tuning override).

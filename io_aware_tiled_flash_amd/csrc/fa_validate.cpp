@@ -378,7 +378,7 @@ int prepare_bwd(const BwdCall& a, BwdParams* out, std::string* err) {
   p.n_sink = (p.window == 0) ? 0 : (int)(a.n_sink < S ? a.n_sink : S);
   p.scale = a.scale;
   p.c = (float)((double)a.scale * 1.4426950408889634);
-  p.dkv_pair = bwd_dkv_pair(nb * (B * H_kv), a.causal != 0, p.window > 0, a.alibi != nullptr);
+  p.dkv_pair = bwd_dkv_pair(nb * (B * H_kv), a.causal != 0, p.window > 0);
   return FA_OK;
 }
 
@@ -397,17 +397,17 @@ int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, in
   const int64_t nb = S / kBwdRows + (S % kBwdRows != 0);
   const int64_t kv = B * H_kv;
   const int64_t grid = kv > INT64_MAX / nb ? INT64_MAX : nb * kv;
-  const bool pair = bwd_dkv_pair(grid, causal != 0, window > 0 && window < S, alibi != 0);
+  const bool pair = bwd_dkv_pair(grid, causal != 0, window > 0 && window < S);
   const std::string t = std::string("<") + (dtype == kDtypeF16 ? "f16" : "bf16") + ",D=" +
-                        std::to_string(D) + ">";
+                        std::to_string(D) + (alibi ? ",alibi" : "") + ">";
   *name = "fa_bwd_dq_kernel" + t + " (128 rows, 4 waves) + " +
           (pair ? "fa_bwd_dkv2_kernel" + t + " (128 keys, 4 waves, 2 work-groups per CU)"
                 : "fa_bwd_dkv_kernel" + t + " (128 keys, 4 waves, 1 work-group per CU)");
   return FA_OK;
 }
 
-bool bwd_dkv_pair(int64_t grid, bool causal, bool window, bool alibi) {
-  bool pair = !alibi && !window && (grid >= 1024 || (!causal && grid >= 512));
+bool bwd_dkv_pair(int64_t grid, bool causal, bool window) {
+  bool pair = !window && (grid >= 1024 || (!causal && grid >= 512));
   if (const char* e = std::getenv("FLASH_ATTN_DKV")) {
     if (e[0] == '1') pair = false;
     if (e[0] == '2') pair = true;

@@ -397,8 +397,7 @@ def test_bwd_noalloc_unsupported_types():
 def test_backward_kernel_choice(monkeypatch):
     """The dK/dV kernel of a backward: two 4-wave work-groups per CU on grids
     of at least 1024 work-groups of 128 keys (512 without the causal mask),
-    with neither ALiBi nor a window; else one per CU. FLASH_ATTN_DKV=1|2
-    overrides."""
+    and no window; else one per CU. FLASH_ATTN_DKV=1|2 overrides."""
     monkeypatch.delenv("FLASH_ATTN_DKV", raising=False)
     bk = fa.flash_attn_bwd_kernel
     head = bk(4, 16, 4096, 128, fa.FA_BF16, causal=True)
@@ -406,7 +405,9 @@ def test_backward_kernel_choice(monkeypatch):
     assert "dkv2" in bk(2, 16, 2048, 128, fa.FA_BF16, causal=False)          # 512, no mask
     assert "dkv2" not in bk(1, 16, 4096, 128, fa.FA_BF16, causal=True)       # 512, causal
     assert "dkv2" not in bk(4, 16, 4096, 128, fa.FA_BF16, H_kv=2, causal=True)   # 256
-    assert "dkv2" not in bk(4, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)
+    al = bk(4, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)
+    assert "fa_bwd_dq_kernel<bf16,D=128,alibi>" in al and "fa_bwd_dkv2_kernel<bf16,D=128,alibi>" in al, al
+    assert "dkv2" not in bk(1, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)   # 512
     assert "dkv2" not in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=1024)
     assert "dkv2" in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=8192)   # no-op window
     monkeypatch.setenv("FLASH_ATTN_DKV", "2")
