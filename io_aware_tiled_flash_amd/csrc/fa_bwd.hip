@@ -396,6 +396,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
         pT = Tr::mma(va[s], df[s], pT);
       }
       lds_mfma_pipeline<2 * NS, 1, 4>();
+      // kept iff e <= hi and (e >= lo or e <= sk), as one bit word
+      const uint32_t mw = MASK ? keep_word(lo, hi, min(sk, hi), 32 * t) : 0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int e = 32 * t + 8 * (r >> 2) + (r & 3);
@@ -405,7 +407,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         else
           x = __builtin_fmaf(sT[r], p.c, -lse2);
         float pr = fast_exp2(x);
-        if (MASK) pr = ((e <= hi) & ((e >= lo) | (e <= sk))) ? pr : 0.f;
+        if (MASK) pr = keep_or(pr, mw, 8 * (r >> 2) + (r & 3), 0u);
         sT[r] = pr * (pT[r] - delta);   // dS^T
       }
       v8 dsb[2];
@@ -579,7 +581,7 @@ void fa_bwd_dkv_kernel(BwdParams p) {
     }
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
     const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
-    const int ewin = emin + wlen;
+    const int ehi = sinkj ? big : emin + wlen - 1;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f32x16 sc, dp;
@@ -612,6 +614,7 @@ void fa_bwd_dkv_kernel(BwdParams p) {
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       f32x16 pm, ds;
+      const uint32_t mw = MASK ? keep_word(emin, ehi, -1, 32 * t) : 0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int g = r >> 2, e4 = r & 3;
@@ -622,7 +625,7 @@ void fa_bwd_dkv_kernel(BwdParams p) {
         else
           x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
         float pr = fast_exp2(x);
-        if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
+        if (MASK) pr = keep_or(pr, mw, 8 * g + e4, 0u);
         pm[r] = pr;
         ds[r] = pr * (dp[r] - dd[g][e4]);
       }
@@ -803,7 +806,7 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
     }
     const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
     const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
-    const int ewin = emin + wlen;
+    const int ehi = sinkj ? big : emin + wlen - 1;
     // The LDS offsets pass through an empty asm each step, so the read
     // addresses are formed here (one add each) instead of being hoisted out
     // of the loop, where 30-odd of them do not fit the register budget.
@@ -855,6 +858,7 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
     // this lane's rows of the block: 8 g + 4 h + (0..3); with ALiBi their
     // lse2 / delta are read one group of four at a time, pinned (all 32 at
     // once ran that build out of registers)
+    const uint32_t mw = MASK ? keep_word(emin, ehi, -1, 0) : 0u;
     f32x4 l2[4], dd[4];
     const auto read_rows = [&](int g) {
       l2[g] = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * h);
@@ -877,7 +881,7 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
         else
           x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
         float pr = fast_exp2(x);
-        if (MASK) pr = ((e >= emin) & ((e < ewin) | sinkj)) ? pr : 0.f;
+        if (MASK) pr = keep_or(pr, mw, e, 0u);
         sc[r] = pr;                        // P
         dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
       }

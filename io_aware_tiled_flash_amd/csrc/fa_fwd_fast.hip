@@ -156,16 +156,16 @@ struct Core {
     const int jb = k0 + 4 * h;
     const int hi = (p.causal ? min(i, p.S - 1) : p.S - 1) - jb;
     if (p.window > 0) {
+      // kept iff e <= hi and (e >= lo or e <= sk): one bit word per sub-tile
       const int lo = i - p.window + 1 - jb;
-      const int sk = p.n_sink - 1 - jb;
+      const int skh = min(p.n_sink - 1 - jb, hi);
 #pragma unroll
-      for (int t = 0; t < NTU; ++t)
+      for (int t = 0; t < NTU; ++t) {
+        const uint32_t w = keep_word(lo, hi, skh, 32 * t);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int e = 32 * t + 8 * (r >> 2) + (r & 3);
-          const bool keep = (e <= hi) & ((e >= lo) | (e <= sk));
-          acc[t][r] = keep ? acc[t][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          acc[t][r] = keep_or(acc[t][r], w, 8 * (r >> 2) + (r & 3), 0xff800000u);
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < NTU; ++t)

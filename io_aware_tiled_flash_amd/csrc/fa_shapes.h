@@ -143,10 +143,11 @@ struct BwdParams {
 // The dK/dV kernel of a backward: two 4-wave work-groups per CU (K in
 // registers, V in LDS, 32-row query tiles) when the grid fills the chip
 // well, else one work-group per CU with K and V in registers. Measured on
-// gfx950: the pair wins by 5-11 % on grids of 1024 work-groups and more
-// without a window (ALiBi included), and by 5 % on a 512-work-group grid
-// without the causal mask; it loses under a window, on a single causal round
-// of 512 work-groups (imbalance) and on smaller grids.
+// gfx950: the pair wins by 2-23 % on grids of 1024 work-groups and more
+// (ALiBi and windows included), and by 5-8 % on 512-work-group grids whose
+// key blocks see equal work (no causal mask, or a window); it loses on a
+// single causal round of 512 work-groups (the first key blocks see every
+// query block) and on smaller grids.
 // FLASH_ATTN_DKV=1|2 forces one (tuning, tests).
 bool bwd_dkv_pair(int64_t grid, bool causal, bool window);
 

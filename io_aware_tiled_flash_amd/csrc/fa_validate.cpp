@@ -407,7 +407,7 @@ int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, in
 }
 
 bool bwd_dkv_pair(int64_t grid, bool causal, bool window) {
-  bool pair = !window && (grid >= 1024 || (!causal && grid >= 512));
+  bool pair = grid >= 1024 || ((!causal || window) && grid >= 512);
   if (const char* e = std::getenv("FLASH_ATTN_DKV")) {
     if (e[0] == '1') pair = false;
     if (e[0] == '2') pair = true;

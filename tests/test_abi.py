@@ -396,8 +396,8 @@ def test_bwd_noalloc_unsupported_types():
 
 def test_backward_kernel_choice(monkeypatch):
     """The dK/dV kernel of a backward: two 4-wave work-groups per CU on grids
-    of at least 1024 work-groups of 128 keys (512 without the causal mask),
-    and no window; else one per CU. FLASH_ATTN_DKV=1|2 overrides."""
+    of at least 1024 work-groups of 128 keys (512 without the causal mask or
+    with a window); else one per CU. FLASH_ATTN_DKV=1|2 overrides."""
     monkeypatch.delenv("FLASH_ATTN_DKV", raising=False)
     bk = fa.flash_attn_bwd_kernel
     head = bk(4, 16, 4096, 128, fa.FA_BF16, causal=True)
@@ -408,8 +408,10 @@ def test_backward_kernel_choice(monkeypatch):
     al = bk(4, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)
     assert "fa_bwd_dq_kernel<bf16,D=128,alibi>" in al and "fa_bwd_dkv2_kernel<bf16,D=128,alibi>" in al, al
     assert "dkv2" not in bk(1, 16, 4096, 128, fa.FA_BF16, causal=True, alibi=True)   # 512
-    assert "dkv2" not in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=1024)
-    assert "dkv2" in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=8192)   # no-op window
+    assert "dkv2" in bk(2, 16, 8192, 128, fa.FA_BF16, causal=True, window=1024)    # 2048
+    assert "dkv2" in bk(1, 8, 8192, 128, fa.FA_BF16, causal=True, window=4096)     # 512
+    assert "dkv2" not in bk(1, 4, 8192, 128, fa.FA_BF16, causal=True, window=1024)  # 256
+    assert "dkv2" not in bk(1, 8, 8192, 128, fa.FA_BF16, causal=True, window=8192)  # no-op window
     monkeypatch.setenv("FLASH_ATTN_DKV", "2")
     assert "dkv2" in bk(1, 1, 64, 64, fa.FA_F16, causal=True)
     monkeypatch.setenv("FLASH_ATTN_DKV", "1")
