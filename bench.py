@@ -66,15 +66,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "079757b2280e928474072b9313e843e76505547ef86bbc8373f7979395122a4c"): 873258803,
+     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 857298125,
     ("causal_b1h32s16384d128_bf16",
-     "079757b2280e928474072b9313e843e76505547ef86bbc8373f7979395122a4c"): 1611653837,
+     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 1582800589,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "079757b2280e928474072b9313e843e76505547ef86bbc8373f7979395122a4c"): 2202021478,
+     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 2240196301,
     ("noncausal_b2h8s1024d64_f16",
-     "079757b2280e928474072b9313e843e76505547ef86bbc8373f7979395122a4c"): 9364685,
+     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 9148006,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "000d0fd7abaaf78ea0d82cee36aeb535dac0b698eb92da6aadf06dccd8dac7f6"): 1652447130,
+     "31ef30a093aabd751f7b9ac5517ecfc092ba21d422815e3ea0035416787fb476"): 1803497472,
 }
 
 
