@@ -66,15 +66,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 857298125,
+     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 857298125,
     ("causal_b1h32s16384d128_bf16",
-     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 1582800589,
+     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 1582800589,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 2240196301,
+     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 2240196301,
     ("noncausal_b2h8s1024d64_f16",
-     "a26e7c8756073861d5664ccad5693c56740a13f92b955b4b23f528d72fef37dd"): 9148006,
+     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 9148006,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "31ef30a093aabd751f7b9ac5517ecfc092ba21d422815e3ea0035416787fb476"): 1803497472,
+     "f3d0ecd273b6185c2459f95e6f3699e23c5fae9f79a43ff97df7fbfad0e48edd"): 1803497472,
 }
 
 

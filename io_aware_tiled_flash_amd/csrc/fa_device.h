@@ -64,22 +64,10 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Per-lane bit word of a partially visible block's kept keys, for masks
-// with a window: bit p stands for key offset base + p of the lane's key
-// numbering, and the kept offsets are [lo, hi] plus those <= skh (the sinks,
-// already capped at hi). Clamped bounds make any of them empty. A score is
-// then kept or replaced with two instructions (keep_or) instead of three
-// compares and two lane-mask operations.
-__device__ __forceinline__ uint32_t ones_below(int n) {   // n in [0, 32]
-  return (uint32_t)(0xffffffffull >> (32 - n));
-}
-__device__ __forceinline__ int clamp32(int x) { return min(max(x, 0), 32); }
-__device__ __forceinline__ uint32_t keep_word(int lo, int hi, int skh, int base) {
-  return (ones_below(clamp32(hi - base + 1)) & ~ones_below(clamp32(lo - base))) |
-         ones_below(clamp32(skh - base + 1));
-}
-// x if bit p of w is set, else the float with bits `fill`: a signed 1-bit
-// extract (0 or all ones) and one bit select.
+// x if bit p of the kept-key word w (keep_word) is set, else the float with
+// bits `fill`: a signed 1-bit extract (0 or all ones) and one bit select --
+// two instructions per score instead of three compares and two lane-mask
+// operations.
 __device__ __forceinline__ float keep_or(float x, uint32_t w, int p, uint32_t fill) {
   const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)w, p, 1);
   return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & m) | (fill & ~m));

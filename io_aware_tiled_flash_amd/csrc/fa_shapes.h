@@ -39,6 +39,19 @@ struct StepRange {
   int lo, hi;   // steps [lo, hi)
 };
 
+// Per-lane bit word of a partially visible block's kept keys, for masks with
+// a window: bit p (0..31) stands for offset base + p of the lane's key (or
+// row) numbering, and the kept offsets are [lo, hi] plus those <= skh (the
+// sinks; empty for skh < base). Clamped bounds make any part empty.
+constexpr uint32_t ones_below(int n) {   // n in [0, 32]
+  return (uint32_t)(0xffffffffull >> (32 - n));
+}
+constexpr int clamp32(int x) { return cmin(cmax(x, 0), 32); }
+constexpr uint32_t keep_word(int lo, int hi, int skh, int base) {
+  return (ones_below(clamp32(hi - base + 1)) & ~ones_below(clamp32(lo - base))) |
+         ones_below(clamp32(skh - base + 1));
+}
+
 // Forward (and dQ): query rows [q_lo, q_lo + BR), key blocks of BC keys; the
 // walk visits n_sinkb sink blocks, then key blocks kb_lo .. kb_hi. Key block
 // kb is fully visible when its keys end at or before the sequence end, and

@@ -309,6 +309,47 @@ int main() {
            "tile c3");
   }
 
+  // ---- kept-key bit words of the masks with a window ----
+  // keep_word bit by bit against the set it stands for, and the two masks the
+  // kernels build from it: forward / dQ (key offset e kept iff e <= hi and
+  // (e >= lo or e <= sk)) with skh = min(sk, hi), and dK/dV (row offset e kept
+  // iff e >= emin and (e < emin + wlen or the key is a sink)) with
+  // hi = sink ? 2^30 : emin + wlen - 1.
+  {
+    Rng g{4242};
+    const int big = 1 << 30;
+    int words = 0;
+    auto near = [&](int base) {   // bounds around the word, now and then far away
+      switch (g.next() % 8) {
+        case 0: return -big;
+        case 1: return big;
+        case 2: return base + (int)(g.next() % 4000) - 2000;
+        default: return base + (int)(g.next() % 80) - 24;
+      }
+    };
+    for (int trial = 0; trial < 200000; ++trial) {
+      const int base = 32 * ((int)(g.next() % 64) - 32);
+      const int lo = near(base), hi = near(base), sk = near(base);
+      const uint32_t w = fa::keep_word(lo, hi, sk, base);
+      const uint32_t wf = fa::keep_word(lo, hi, std::min(sk, hi), base);
+      const int emin = near(base), wlen = 1 + (int)(g.next() % 300);
+      const bool sink = g.next() % 2;
+      const uint32_t wk = fa::keep_word(emin, sink ? big : emin + wlen - 1, -big, base);
+      bool ok = true;
+      for (int p = 0; p < 32; ++p) {
+        const long e = (long)base + p;
+        ok = ok && (((w >> p) & 1u) == (uint32_t)((lo <= e && e <= hi) || e <= sk));
+        ok = ok && (((wf >> p) & 1u) == (uint32_t)(e <= hi && (e >= lo || e <= sk)));
+        ok = ok && (((wk >> p) & 1u) == (uint32_t)(e >= emin && (e < (long)emin + wlen || sink)));
+      }
+      expect(ok, "keep_word (lo " + std::to_string(lo) + ", hi " + std::to_string(hi) + ", sk " +
+                     std::to_string(sk) + ", base " + std::to_string(base) + ", emin " +
+                     std::to_string(emin) + ", wlen " + std::to_string(wlen) + ")");
+      ++words;
+    }
+    std::printf("keep_word: %d words checked bit by bit\n", words);
+  }
+
   // ---- closed-form mask segments against a scan of the blocks ----
   // The kernels take their fully visible run of blocks from full_key_steps /
   // full_query_steps. Every step of that run must be fully visible, and
