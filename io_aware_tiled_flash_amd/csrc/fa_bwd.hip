@@ -378,11 +378,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
     // scores held at once).
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      // dP^T accumulates from -delta (a per-lane constant here), so the
+      // subtraction of dS = P (dP - delta) happens in the MFMA chain
       f32x16 sT, pT;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sT[r] = 0.f;
-        pT[r] = 0.f;
+        pT[r] = -delta;
       }
       v8 ka[NS], va[NS];
 #pragma unroll
@@ -408,7 +410,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
           x = __builtin_fmaf(sT[r], p.c, -lse2);
         float pr = fast_exp2(x);
         if (MASK) pr = keep_or(pr, mw, 8 * (r >> 2) + (r & 3), 0u);
-        sT[r] = pr * (pT[r] - delta);   // dS^T
+        sT[r] = pr * pT[r];   // dS^T
       }
       v8 dsb[2];
       dsb[0] = pack8<T>(sT, 0);
