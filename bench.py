@@ -66,13 +66,13 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 857298125,
+     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 857298125,
     ("causal_b1h32s16384d128_bf16",
-     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 1582800589,
+     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 1582800589,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 2240196301,
+     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 2240196301,
     ("noncausal_b2h8s1024d64_f16",
-     "0cde2c7f4613acaca67b3faf6748371c4950a2fa58b2a53f977b770918b31fce"): 9148006,
+     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 9148006,
     ("bwd_causal_b4h16s4096d128_bf16",
      "f3d0ecd273b6185c2459f95e6f3699e23c5fae9f79a43ff97df7fbfad0e48edd"): 1803497472,
 }

@@ -20,30 +20,9 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 16-byte chunk swizzle of the K layout: logical chunk c of a row sits at
-// c ^ k_swz(row). LDS serves 256 bytes a clock from 64 four-byte banks, so a
-// 16-byte read serves 16 lanes a cycle and an 8-byte read 32. The tile is
-// read two ways:
-//  * rows (an MFMA operand over d): 16 consecutive rows, one logical chunk,
-//    in a cycle -- the 16 rows must land in different banks;
-//  * transposed (ds_read_b64_tr_b16): 4 consecutive rows x logical chunks
-//    4 dt .. 4 dt + 3 in a cycle -- the 4 rows must land in different groups
-//    of four chunks.
-// At D = 128 (256-byte rows) row bits 0-1 go to chunk bits 2-3 and row bits
-// 2-3 to chunk bits 0-1. At D = 64 (128-byte rows) rows 2m and 2m + 1 already
-// sit in opposite bank halves: row bit 1 goes to chunk bit 2 and row bits 2-3
-// to chunk bits 0-1. (A plain row & 15 / (row >> 1) & 7 keeps the 4 rows of
-// a transposing read in one group of chunks: 4- / 2-way bank conflicts.)
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
-                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
-}
-// 64-byte segment swizzle of the V layout.
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  return D == 128 ? (row & 3) : ((row >> 1) & 1);
-}
+// The K layout's chunk swizzle k_swz and the V layout's segment swizzle
+// v_swz are in fa_shapes.h (constexpr, so the host unit can check that every
+// read pattern below is free of bank conflicts).
 
 // Direct HBM -> LDS copy of one BC x D tile (K if IS_V is false, else V)
 // with buffer loads: wave w fills LDS 16-byte positions [w*NI*64,

@@ -39,6 +39,33 @@ struct StepRange {
   int lo, hi;   // steps [lo, hi)
 };
 
+// ---- LDS layouts of the bf16/f16 tiles ----
+//
+// 16-byte chunk swizzle of the K layout: logical chunk c of a row sits at
+// c ^ k_swz(row). LDS serves 256 bytes a clock from 64 four-byte banks, so a
+// 16-byte read serves 16 lanes a cycle and an 8-byte read 32. The tile is
+// read two ways:
+//  * rows (an MFMA operand over d): 16 consecutive rows, one logical chunk,
+//    in a cycle -- the 16 rows must land in different banks;
+//  * transposed (ds_read_b64_tr_b16): 4 consecutive rows x logical chunks
+//    4 dt .. 4 dt + 3 in a cycle -- the 4 rows must land in different groups
+//    of four chunks.
+// At D = 128 (256-byte rows) row bits 0-1 go to chunk bits 2-3 and row bits
+// 2-3 to chunk bits 0-1. At D = 64 (128-byte rows) rows 2m and 2m + 1 already
+// sit in opposite bank halves: row bit 1 goes to chunk bit 2 and row bits 2-3
+// to chunk bits 0-1. (A plain row & 15 / (row >> 1) & 7 keeps the 4 rows of
+// a transposing read in one group of chunks: 4- / 2-way bank conflicts.)
+template <int D>
+constexpr int k_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+// 64-byte segment swizzle of the V layout.
+template <int D>
+constexpr int v_swz(int row) {
+  return D == 128 ? (row & 3) : ((row >> 1) & 1);
+}
+
 // Per-lane bit word of a partially visible block's kept keys, for masks with
 // a window: bit p (0..31) stands for offset base + p of the lane's key (or
 // row) numbering, and the kept offsets are [lo, hi] plus those <= skh (the

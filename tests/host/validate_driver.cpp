@@ -13,6 +13,7 @@
 #include <limits>
 #include <string>
 #include <vector>
+#include <type_traits>
 
 #include "../../include/flash_attn.h"
 #include "../../io_aware_tiled_flash_amd/csrc/fa_validate.h"
@@ -307,6 +308,93 @@ int main() {
     expect(fa::tile_shape(1, 1, 64, 48, FA_BF16, &bq, &bk, &err) == FA_ERR_UNSUPPORTED, "tile d48");
     expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, &bq, &bk, &err) == FA_OK && bk == fa::kFastBC,
            "tile c3");
+  }
+
+  // ---- LDS layouts: every read pattern free of bank conflicts ----
+  // gfx950 LDS: 64 banks of 4 bytes, 256 bytes a clock; a 16-byte read serves
+  // 16 lanes a cycle, an 8-byte read 32. An instruction is conflict-free when
+  // no bank holds two different dwords within a cycle's lanes. The lane
+  // addresses restate the kernels' offsets: K-layout row reads (forward QK,
+  // every backward operand over d), K-layout transposing reads (dQ's K^T,
+  // dK/dV's Q^T and dO^T) and the forward's V-layout transposing reads.
+  {
+    auto cycles = [](const std::vector<long>& byte_addr, int width) {
+      const int per = 256 / width;
+      int tot = 0;
+      for (int g0 = 0; g0 < 64; g0 += per) {
+        std::vector<std::vector<long>> bank(64);
+        for (int l = g0; l < g0 + per; ++l)
+          for (int w = 0; w < width / 4; ++w) {
+            const long dw = byte_addr[l] / 4 + w;
+            auto& b = bank[dw % 64];
+            if (std::find(b.begin(), b.end(), dw) == b.end()) b.push_back(dw);
+          }
+        size_t worst = 0;
+        for (auto& b : bank) worst = std::max(worst, b.size());
+        tot += (int)worst;
+      }
+      return tot;
+    };
+    auto check = [&](auto dc) {
+      constexpr int D = decltype(dc)::value;
+      const long E = 2;   // bf16 / f16 bytes
+      std::vector<long> a(64);
+      for (int t = 0; t < 4; ++t)          // row reads: lane (col, h), rows 32 t + col
+        for (int s = 0; s < D / 16; ++s) {
+          for (int l = 0; l < 64; ++l) {
+            const int row = 32 * t + (l & 31), h = l >> 5;
+            a[l] = E * (row * D + (((2 * s + h) ^ fa::k_swz<D>(row)) << 3));
+          }
+          expect(cycles(a, 16) == 4, "k_swz row read conflicts, D " + std::to_string(D));
+        }
+      for (int u = 0; u < 8; ++u)          // transposing reads of the K layout
+        for (int part = 0; part < 2; ++part)
+          for (int dt = 0; dt < D / 32; ++dt) {
+            for (int l = 0; l < 64; ++l) {
+              const int h = l >> 5, grp = (l >> 4) & 1, r16 = l & 15;
+              const int row = 16 * u + 4 * h + (r16 >> 2) + 8 * part;
+              const int chunk = 4 * dt + 2 * grp + ((r16 & 3) >> 1);
+              a[l] = E * (row * D + ((chunk ^ fa::k_swz<D>(row)) << 3) + 4 * (r16 & 1));
+            }
+            expect(cycles(a, 8) == 2, "k_swz transposing read conflicts, D " + std::to_string(D));
+          }
+      for (int tu = 0; tu < 4; ++tu)       // transposing reads of the V layout
+        for (int part = 0; part < 2; ++part)
+          for (int dt = 0; dt < D / 32; ++dt) {
+            for (int l = 0; l < 64; ++l) {
+              const int h = l >> 5, grp = (l >> 4) & 1, r16 = l & 15;
+              const int row = 16 * tu + 4 * h + (r16 >> 2) + 8 * part;
+              a[l] = E * (row * D + 16 * grp + 4 * (r16 & 3) + ((dt ^ fa::v_swz<D>(row)) << 5));
+            }
+            expect(cycles(a, 8) == 2, "v_swz transposing read conflicts, D " + std::to_string(D));
+          }
+      // each swizzle is a permutation of a row's chunks / segments
+      for (int row = 0; row < 128; ++row) {
+        std::vector<int> seen(D / 8, 0), segs(D / 32, 0);
+        for (int c = 0; c < D / 8; ++c) {
+          const int p = c ^ fa::k_swz<D>(row);
+          expect(0 <= p && p < D / 8 && !seen[p]++, "k_swz not a permutation");
+        }
+        for (int sg = 0; sg < D / 32; ++sg) {
+          const int p = sg ^ fa::v_swz<D>(row);
+          expect(0 <= p && p < D / 32 && !segs[p]++, "v_swz not a permutation");
+        }
+      }
+    };
+    check(std::integral_constant<int, 128>{});
+    check(std::integral_constant<int, 64>{});
+    // the model itself: a plain row & 15 swizzle gives the 4-way conflicts
+    // the counters showed on the transposing reads
+    {
+      std::vector<long> a(64);
+      for (int l = 0; l < 64; ++l) {
+        const int h = l >> 5, grp = (l >> 4) & 1, r16 = l & 15;
+        const int row = 4 * h + (r16 >> 2), chunk = 2 * grp + ((r16 & 3) >> 1);
+        a[l] = 2 * (row * 128 + ((chunk ^ (row & 15)) << 3) + 4 * (r16 & 1));
+      }
+      expect(cycles(a, 8) == 8, "bank model: row & 15 should give 4-way conflicts");
+    }
+    std::printf("LDS layouts: row and transposing reads conflict-free at D 64 and 128\n");
   }
 
   // ---- kept-key bit words of the masks with a window ----
