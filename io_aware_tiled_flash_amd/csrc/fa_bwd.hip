@@ -176,42 +176,47 @@ __device__ __forceinline__ void rows_to_lds(float* lds, const float* g, int lane
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, (uint32_t)lane * 4u, 0, 0, 0);
 }
 
-// RowOffsets in two registers: the chunk index 2 s + h and the row swizzle
-// share no bits above bit 0 of the swizzle, so (2 s + h) ^ sw = ((2 s) ^ sh)
-// + (h ^ (sw & 1)) with sh = sw & ~1, and off(s) = base + ((16 s) ^ (sh << 3))
-// costs one XOR with a constant per k-step instead of a register per k-step.
+// Row reads (the A operand of an MFMA over d) in byte form, for 2-byte
+// elements: lane (col, h) reads chunk (2 s + h) ^ k_swz(row) of row
+// row0 + col. The row's offset, the swizzled chunk h ^ k_swz and the
+// k-step's chunk bits 2 s occupy disjoint bit fields once the low two are
+// XORed, so the byte offset of k-step s is b ^ (32 s): one XOR per k-step.
+// Rows 32 apart share the swizzle, and 32 rows of D elements span a
+// multiple of 256 bytes, so another wave's rows are b + 64 D wave.
 template <int D>
-struct RowOffsets2 {
-  int base, sh8;
+struct RowXor {
+  uint32_t b;
   __device__ __forceinline__ void init(int lane) {
     const int h = lane >> 5, col = lane & 31;
-    const int sw = k_swz<D>(col);
-    base = col * D + ((h ^ (sw & 1)) << 3);
-    sh8 = (sw & ~1) << 3;
+    b = (uint32_t)(2 * (col * D + ((h ^ k_swz<D>(col)) << 3)));
   }
-  __device__ __forceinline__ int off(int s) const { return base + ((16 * s) ^ sh8); }
+  __device__ __forceinline__ uint32_t at(int s) const { return b ^ (32u * (uint32_t)s); }
 };
 
-// TrOffsets in four registers, by the same split: the chunk index 4 dt + c
-// (c < 4) and the swizzle share no bits above bit 1, so lo / hi (dt) =
-// base + ((32 dt) ^ (swizzle & ~3) << 3) for the row of either half.
+// Transposing reads (see TrOffsets) in byte form, by the same argument:
+// chunk (4 dt + c) ^ k_swz(row) with c < 4, so lo / hi (dt) = b[0] / b[1]
+// ^ (64 dt).
 template <int D>
-struct TrOffsets2 {
-  int base[2], sh8[2];
+struct TrXor {
+  uint32_t b[2];
   __device__ __forceinline__ void init(int lane) {
     const int h = lane >> 5, grp = (lane >> 4) & 1, r16 = lane & 15;
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
       const int row = 4 * h + (r16 >> 2) + 8 * part;
-      const int sw = k_swz<D>(row);
       const int c = 2 * grp + ((r16 & 3) >> 1);
-      base[part] = row * D + ((c ^ (sw & 3)) << 3) + 4 * (r16 & 1);
-      sh8[part] = (sw & ~3) << 3;
+      b[part] = (uint32_t)(2 * (row * D + ((c ^ k_swz<D>(row)) << 3) + 4 * (r16 & 1)));
     }
   }
-  __device__ __forceinline__ int lo(int dt) const { return base[0] + ((32 * dt) ^ sh8[0]); }
-  __device__ __forceinline__ int hi(int dt) const { return base[1] + ((32 * dt) ^ sh8[1]); }
+  __device__ __forceinline__ uint32_t lo(int dt) const { return b[0] ^ (64u * (uint32_t)dt); }
+  __device__ __forceinline__ uint32_t hi(int dt) const { return b[1] ^ (64u * (uint32_t)dt); }
 };
+
+// p advanced by b bytes
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const T* p, uint32_t b) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + b);
+}
 
 // Direct-to-LDS copy of ROWS rows of D elements (K layout: 16-byte chunks
 // XOR-swizzled by row, as TileDma) by NW waves. Rows past the sequence end
@@ -736,9 +741,11 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
   const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + kv_head;
   const T* __restrict__ Vh = uniform_ptr(reinterpret_cast<const T*>(p.v) + kv_head);
 
-  RowOffsets2<D> ro;
+  static_assert(sizeof(T) == 2, "byte-form LDS offsets assume 2-byte elements");
+  RowXor<D> ro;
   ro.init(lane);
-  TrOffsets2<D> tro;
+  const uint32_t vo = ro.b + (uint32_t)(64 * D * wave);   // this wave's 32 rows of V
+  TrXor<D> tro;
   tro.init(lane);
   RowsDma<T, D, BK, 4> vdma;
   vdma.init(wave, lane);
@@ -791,7 +798,6 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
   wait_vmem<0>();
   __syncthreads();
 
-  const T* const kw_v = vs + 32 * wave * D;
   auto step = [&](auto par, auto mask, int it) __attribute__((always_inline)) {
     constexpr int PAR = decltype(par)::value;
     constexpr bool MASK = decltype(mask)::value;
@@ -812,10 +818,11 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
     // The LDS offsets pass through an empty asm each step, so the read
     // addresses are formed here (one add each) instead of being hoisted out
     // of the loop, where 30-odd of them do not fit the register budget.
-    RowOffsets2<D> rl = ro;
-    TrOffsets2<D> tl = tro;
-    asm volatile("" : "+v"(rl.base), "+v"(rl.sh8), "+v"(tl.base[0]), "+v"(tl.base[1]),
-                 "+v"(tl.sh8[0]), "+v"(tl.sh8[1]));
+    RowXor<D> rl = ro;
+    uint32_t vl = vo;
+    TrXor<D> tl = tro;
+    asm volatile("" : "+v"(rl.b), "+v"(vl), "+v"(tl.b[0]), "+v"(tl.b[1]));
+    auto vrow = [&](int s) __attribute__((always_inline)) { return at_bytes(vs, vl ^ (32u * s)); };
     f32x16 sc, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -829,30 +836,30 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
     // the read latency.
     if constexpr (!ALIBI) {
       v8 qa[2], da[2], va[2];
-      qa[0] = lds_row8(qs + rl.off(0));
-      qa[1] = lds_row8(qs + rl.off(1));
-      da[0] = lds_row8(dos + rl.off(0));
-      va[0] = lds_row8(kw_v + rl.off(0));
+      qa[0] = lds_row8(at_bytes(qs, rl.at(0)));
+      qa[1] = lds_row8(at_bytes(qs, rl.at(1)));
+      da[0] = lds_row8(at_bytes(dos, rl.at(0)));
+      va[0] = lds_row8(vrow(0));
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if (s + 1 < NS) {
-          da[(s + 1) & 1] = lds_row8(dos + rl.off(s + 1));
-          va[(s + 1) & 1] = lds_row8(kw_v + rl.off(s + 1));
+          da[(s + 1) & 1] = lds_row8(at_bytes(dos, rl.at(s + 1)));
+          va[(s + 1) & 1] = lds_row8(vrow(s + 1));
         }
         sc = Tr::mma(qa[s & 1], kf[s], sc);
         __builtin_amdgcn_sched_barrier(0);
-        if (s + 2 < NS) qa[s & 1] = lds_row8(qs + rl.off(s + 2));
+        if (s + 2 < NS) qa[s & 1] = lds_row8(at_bytes(qs, rl.at(s + 2)));
         dp = Tr::mma(da[s & 1], va[s & 1], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      v8 qa = lds_row8(qs + rl.off(0));
+      v8 qa = lds_row8(at_bytes(qs, rl.at(0)));
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const v8 da = lds_row8(dos + rl.off(s)), va = lds_row8(kw_v + rl.off(s));
+        const v8 da = lds_row8(at_bytes(dos, rl.at(s))), va = lds_row8(vrow(s));
         sc = Tr::mma(qa, kf[s], sc);
         __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < NS) qa = lds_row8(qs + rl.off(s + 1));
+        if (s + 1 < NS) qa = lds_row8(at_bytes(qs, rl.at(s + 1)));
         dp = Tr::mma(da, va, dp);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -898,8 +905,8 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
     auto tr_reads = [&](int u, int dt, v8& o, v8& q) __attribute__((always_inline)) {
       const T* qq = qs + 16 * u * D;
       const T* oo = dos + 16 * u * D;
-      o = lds_tr8(oo + tl.lo(dt), oo + tl.hi(dt));
-      q = lds_tr8(qq + tl.lo(dt), qq + tl.hi(dt));
+      o = lds_tr8(at_bytes(oo, tl.lo(dt)), at_bytes(oo, tl.hi(dt)));
+      q = lds_tr8(at_bytes(qq, tl.lo(dt)), at_bytes(qq, tl.hi(dt)));
     };
     v8 oT, qT;
     tr_reads(0, 0, oT, qT);
