@@ -74,7 +74,7 @@ MEASURED_TRAFFIC: dict = {
     ("noncausal_b2h8s1024d64_f16",
      "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 9148006,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "f3d0ecd273b6185c2459f95e6f3699e23c5fae9f79a43ff97df7fbfad0e48edd"): 1803497472,
+     "80fc570ffc6da6275bf9a9361e36260179fcca6c8cea15f677aceb798e5f042b"): 1898706637,
 }
 
 
