@@ -117,22 +117,6 @@ __device__ __forceinline__ typename Half16<T>::v8 pack8(const f32x16& acc, int u
   return __builtin_bit_cast(typename Half16<T>::v8, w);
 }
 
-// Store a 32x32 accumulator tile of X^T (rows d, columns = this lane's row r
-// of X) as X[r][32 dt + 8 g + 4 h + 0..3], multiplied by f.
-template <typename T, int D>
-__device__ __forceinline__ void store_rowT(T* __restrict__ dst, const f32x16 (&acc)[D / 32],
-                                           int h, float f) {
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = pack2<T>(acc[dt][4 * g + 0] * f, acc[dt][4 * g + 1] * f);
-      w[1] = pack2<T>(acc[dt][4 * g + 2] * f, acc[dt][4 * g + 3] * f);
-      *reinterpret_cast<u32x2*>(dst + 32 * dt + 8 * g + 4 * h) = w;
-    }
-}
-
 // Query-block range [first, last] whose rows see some key of [k_lo, k_hi].
 __device__ __forceinline__ void query_range(const BwdParams& p, int k_lo, int k_hi, int BQ,
                                             int& first, int& last) {
@@ -384,12 +368,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       // dP^T accumulates from -delta (a per-lane constant here), so the
-      // subtraction of dS = P (dP - delta) happens in the MFMA chain
+      // subtraction of dS = P (dP - delta) happens in the MFMA chain (not with
+      // ALiBi, whose bias terms need the 16 registers that constant takes)
       f32x16 sT, pT;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sT[r] = 0.f;
-        pT[r] = -delta;
+        pT[r] = ALIBI ? 0.f : -delta;
       }
       v8 ka[NS], va[NS];
 #pragma unroll
@@ -415,7 +400,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
           x = __builtin_fmaf(sT[r], p.c, -lse2);
         float pr = fast_exp2(x);
         if (MASK) pr = keep_or(pr, mw, 8 * (r >> 2) + (r & 3), 0u);
-        sT[r] = pr * pT[r];   // dS^T
+        sT[r] = pr * (ALIBI ? pT[r] - delta : pT[r]);   // dS^T
       }
       v8 dsb[2];
       dsb[0] = pack8<T>(sT, 0);
@@ -453,7 +438,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
   segment(std::true_type{}, 0, f0);
   segment(std::false_type{}, f0, f1);
   segment(std::true_type{}, f1, n_iter);
-  if (row_ok) store_rowT<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)i * D, dq, h, p.scale);
+  // dQ rows through the idle K/V tiles (every wave is past the last barrier)
+  rows_out_staged<T, D>(reinterpret_cast<T*>(p.dq) + head + (size_t)(q_lo + 32 * wave) * D,
+                        S - (q_lo + 32 * wave), dq, p.scale,
+                        ((wave >> 1) == 0 ? k0s : v0s) + (wave & 1) * 32 * D, lane);
 }
 
 // ------------------------------------------------------------------------ //
@@ -691,9 +679,14 @@ void fa_bwd_dkv_kernel(BwdParams p) {
       segment(std::true_type{}, b + f1, b + n_q);
     }
   }
-  if (j < S) {
-    store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
-    store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);
+  // dK / dV rows through the idle Q / dO tiles (every wave is past the last
+  // barrier)
+  {
+    const int row0 = k_lo + 32 * wave;
+    rows_out_staged<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)row0 * D, S - row0, dk,
+                          p.scale, q0s + 32 * wave * D, lane);
+    rows_out_staged<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)row0 * D, S - row0, dv,
+                          1.f, d0s + 32 * wave * D, lane);
   }
 }
 
@@ -946,9 +939,15 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
       segment(std::true_type{}, b + f1, b + n_q);
     }
   }
-  if (j < S) {
-    store_rowT<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)j * D, dk, h, p.scale);
-    store_rowT<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)j * D, dv, h, 1.f);
+  // dK rows through this wave's own V rows, dV rows through one Q / dO tile
+  // (every wave is past the last barrier)
+  {
+    const int row0 = k_lo + 32 * wave;
+    rows_out_staged<T, D>(reinterpret_cast<T*>(p.dk) + kv_head + (size_t)row0 * D, S - row0, dk,
+                          p.scale, vs + 32 * wave * D, lane);
+    T* const st = wave == 0 ? q0s : wave == 1 ? d0s : wave == 2 ? q1s : d1s;
+    rows_out_staged<T, D>(reinterpret_cast<T*>(p.dv) + kv_head + (size_t)row0 * D, S - row0, dv,
+                          1.f, st, lane);
   }
 }
 

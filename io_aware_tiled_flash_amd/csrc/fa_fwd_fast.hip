@@ -312,45 +312,15 @@ struct Core {
     }
   }
 
-  // The same through the wave's LDS region `stage` (32 rows of D elements):
-  // each lane writes its 8-byte pieces, then the wave reads whole 16-byte
-  // chunks row by row and writes full rows of O. The region's 8-byte slot of
-  // (row r, chunk c, half e) is ((c ^ sw(r)) << 1) | (e ^ r bit 4), so the
-  // 32 rows of a write cycle meet every bank once, and a read instruction
-  // (4 rows at D = 128, 8 at D = 64) sees one value of r bit 4.
+  // The same through the wave's LDS slice `stage` (32 rows of D elements;
+  // rows_out_staged writes full 16-byte row chunks).
   __device__ __forceinline__ void epilogue_staged(const FwdParams& p, size_t head, int bh,
                                                   T* stage, int row0, int lane) {
-    constexpr int RB = 2 * D;                       // row bytes
-    constexpr int CPR = RB / 16;                    // 16-byte chunks per row
-    constexpr int RPI = 1024 / RB;                  // rows per read instruction
-    auto sw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-    static_assert(sizeof(T) == 2, "16-bit output");
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.f / l_tot;
-    char* const st = reinterpret_cast<char*>(stage);
-    const int r = col;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack2<T>(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-        w[1] = pack2<T>(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-        const int slot = (((4 * dt + g) ^ sw(r)) << 1) | (h ^ ((r >> 4) & 1));
-        *reinterpret_cast<u32x2*>(st + r * RB + slot * 8) = w;
-      }
     if (i < p.S && h == 0) p.lse[(size_t)bh * p.S + i] = (mc + fast_log2(l_tot)) * kLn2;
-    T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head;
-#pragma unroll
-    for (int ii = 0; ii < 32 / RPI; ++ii) {
-      const int lr = ii * RPI + lane / CPR;
-      const int pc = lane % CPR;
-      u32x4 v = *reinterpret_cast<const u32x4*>(st + lr * RB + pc * 16);
-      if (((ii * RPI) >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      const int row = row0 + lr;
-      if (row < p.S)
-        *reinterpret_cast<u32x4*>(Oh + (size_t)row * D + 8 * (pc ^ sw(lr))) = v;
-    }
+    rows_out_staged<T, D>(reinterpret_cast<T*>(p.o) + head + (size_t)row0 * D, p.S - row0, oacc,
+                          inv, stage, lane);
   }
 
   // O = O / l (both lane halves' partial sums), LSE = (mc + log2 l) ln 2.

@@ -77,6 +77,48 @@ struct TileDma {
   }
 };
 
+// A wave's 32 rows of X from a 32x32 accumulator layout (lane (r, h), r =
+// lane & 31, holds X[r][32 dt + 8 g + 4 h + e] in acc[dt][4 g + e]), times
+// `scale`, packed to T and written to dst (row-major, D elements a row; rows
+// r >= nrows are not written) through the wave's LDS slice `stage` (32 D
+// elements). Each lane writes its 8-byte pieces to the slice, then the wave
+// reads whole 16-byte chunks row by row and writes full rows with 16-byte
+// stores, instead of every store instruction touching 32 rows. The slice's
+// 8-byte slot of (row r, chunk c, half e) is ((c ^ sw(r)) << 1) | (e ^ r bit
+// 4), with sw(r) = r & 15 (D = 128) or (r >> 1) & 7 (D = 64): the 32 rows of a
+// write cycle meet every bank once, and each read instruction (4 rows at
+// D = 128, 8 at D = 64) sees one value of r bit 4.
+template <typename T, int D>
+__device__ __forceinline__ void rows_out_staged(T* __restrict__ dst, int nrows,
+                                                const f32x16 (&acc)[D / 32], float scale,
+                                                T* stage, int lane) {
+  static_assert(sizeof(T) == 2 && (D == 64 || D == 128), "16-bit rows of 64 or 128");
+  constexpr int RB = 2 * D;        // row bytes
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;   // rows per read instruction
+  auto sw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  char* const st = reinterpret_cast<char*>(stage);
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = pack2<T>(acc[dt][4 * g + 0] * scale, acc[dt][4 * g + 1] * scale);
+      w[1] = pack2<T>(acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale);
+      const int slot = (((4 * dt + g) ^ sw(r)) << 1) | (h ^ ((r >> 4) & 1));
+      *reinterpret_cast<u32x2*>(st + r * RB + slot * 8) = w;
+    }
+#pragma unroll
+  for (int ii = 0; ii < 32 / RPI; ++ii) {
+    const int lr = ii * RPI + lane / CPR;
+    const int pc = lane % CPR;
+    u32x4 v = *reinterpret_cast<const u32x4*>(st + lr * RB + pc * 16);
+    if (((ii * RPI) >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    if (lr < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)lr * D + 8 * (pc ^ sw(lr))) = v;
+  }
+}
+
 // A wave-uniform pointer moved to scalar registers.
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
