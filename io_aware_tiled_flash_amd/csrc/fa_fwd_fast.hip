@@ -312,6 +312,18 @@ struct Core {
     }
   }
 
+  // The key split's partial through the wave's LDS slice `stage` (32 rows of
+  // D floats; rows_out_staged_f32 writes full 16-byte row chunks).
+  __device__ __forceinline__ void epilogue_partial_staged(const FwdParams& p, int split, int bh,
+                                                          float* stage, int row0, int lane) {
+    const float l_tot = xhalf_sum(l_run);
+    const bool any = l_tot > 0.f;
+    const float inv = any ? 1.f / l_tot : 0.f;
+    const size_t base = ((size_t)split * p.BH + bh) * (size_t)p.S;
+    if (i < p.S && h == 0) p.lse_part[base + i] = any ? (mc + fast_log2(l_tot)) * kLn2 : kNegInf;
+    rows_out_staged_f32<D>(p.o_part + (base + row0) * D, p.S - row0, oacc, inv, stage, lane);
+  }
+
   // The same through the wave's LDS slice `stage` (32 rows of D elements;
   // rows_out_staged writes full 16-byte row chunks).
   __device__ __forceinline__ void epilogue_staged(const FwdParams& p, size_t head, int bh,
@@ -491,7 +503,15 @@ __device__ __forceinline__ void fwd_body(const FwdParams& p, T* k0s, T* v0s, T* 
   segment(std::false_type{}, f0, f1);
   segment(std::true_type{}, f1, n_iter);
   if (p.o_part) {
-    core.epilogue_partial(p, split, bh);
+    if constexpr (NW == 4) {
+      // wave w's 32 rows of fp32 fill K/V tile w (every wave is past the last
+      // barrier)
+      T* const tile = wave == 0 ? k0s : wave == 1 ? v0s : wave == 2 ? k1s : v1s;
+      core.epilogue_partial_staged(p, split, bh, reinterpret_cast<float*>(tile),
+                                   q_lo + 32 * wave, lane);
+    } else {
+      core.epilogue_partial(p, split, bh);
+    }
   } else {
     // every wave is past the last step's barrier: the tiles are free
     T* stage = (wave >> 1) == 0 ? k0s : (wave >> 1) == 1 ? v0s : (wave >> 1) == 2 ? k1s : v1s;

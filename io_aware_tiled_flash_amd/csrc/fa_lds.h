@@ -119,6 +119,39 @@ __device__ __forceinline__ void rows_out_staged(T* __restrict__ dst, int nrows,
   }
 }
 
+// The same for fp32 rows (the key split's partial outputs): lane (r, h)
+// holds the 16-byte chunk 8 dt + 2 g + h of row r. A 16-byte write serves 16
+// lanes (16 rows) a cycle, so the chunk is placed at c ^ (r & 15); a read
+// instruction covers 2 rows (D = 128) or 4 (D = 64) with whole chunks. The
+// slice is 32 rows of D floats.
+template <int D>
+__device__ __forceinline__ void rows_out_staged_f32(float* __restrict__ dst, int nrows,
+                                                    const f32x16 (&acc)[D / 32], float scale,
+                                                    float* stage, int lane) {
+  static_assert(D == 64 || D == 128, "rows of 64 or 128 floats");
+  constexpr int RB = 4 * D;        // row bytes
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;   // rows per read instruction
+  char* const st = reinterpret_cast<char*>(stage);
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 w = {acc[dt][4 * g + 0] * scale, acc[dt][4 * g + 1] * scale,
+                       acc[dt][4 * g + 2] * scale, acc[dt][4 * g + 3] * scale};
+      const int c = 8 * dt + 2 * g + h;
+      *reinterpret_cast<f32x4*>(st + r * RB + 16 * (c ^ (r & 15))) = w;
+    }
+#pragma unroll
+  for (int ii = 0; ii < 32 / RPI; ++ii) {
+    const int lr = ii * RPI + lane / CPR;
+    const int pc = lane % CPR;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(st + lr * RB + pc * 16);
+    if (lr < nrows) *reinterpret_cast<f32x4*>(dst + (size_t)lr * D + 4 * (pc ^ (lr & 15))) = v;
+  }
+}
+
 // A wave-uniform pointer moved to scalar registers.
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
