@@ -66,15 +66,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 857298125,
+     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 874698547,
     ("causal_b1h32s16384d128_bf16",
-     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 1582800589,
+     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 1632249446,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 2240196301,
+     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 2240363725,
     ("noncausal_b2h8s1024d64_f16",
-     "8487f7fb1212b701ea81d3a1f1d9305d7c87737e104e301041d31f6329b6b62e"): 9148006,
+     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 9124454,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "80fc570ffc6da6275bf9a9361e36260179fcca6c8cea15f677aceb798e5f042b"): 1898706637,
+     "58f17dac447e74ac555445813dad4958c6948d9b76a9c6e425f25cf308ed2bd3"): 1870238925,
 }
 
 
