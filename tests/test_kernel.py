@@ -107,7 +107,18 @@ def test_workload_parity(name):
     assert o.shape == q.shape and o.dtype == q.dtype and lse.shape == q.shape[:3]
     al = None if slopes is None else slopes.astype(np.float64)
     small = w.B * w.H * w.S <= 32768
-    if small:
+    if name == fa_inputs.HEADLINE:
+        # every head and row of the headline shape, the oracle on a pool of
+        # single-threaded processes (the same code as the bench line's parity)
+        import bench
+        _say(f"workload {name}: oracle on all {w.B * w.H} heads")
+        _, heads, res = bench.cpu_baseline(w, q, k, v, w.B * w.H)
+        par = bench.parity(w, heads, res, (o, lse))
+        _say(f"  {name} (all rows): max|dO|={par['max_abs_dO']:.3e} (tol {par['tol_O']:g})  "
+             f"max rel dLSE={par['max_rel_dLSE']:.3e}")
+        assert len(heads) == w.B * w.H and par["rows_per_head"] == w.S
+        assert par["max_abs_dO"] <= TOL_O[w.dtype] and par["max_rel_dLSE"] <= TOL_LSE_REL, par
+    elif small:
         compare(o, lse, q, k, v, w.dtype, causal=w.causal, scale=w.scale, window=w.window,
                 n_sink=w.n_sink, label=name, alibi=al)
     else:
@@ -258,6 +269,44 @@ def test_random_configurations():
         compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, window=window,
                 n_sink=n_sink, label=label, tol_o=tol,
                 alibi=None if slopes is None else slopes.astype(np.float64))
+
+
+def test_random_configurations_sharp_rows():
+    """The sweep above with scales of 1.5 to 8 times 1/sqrt(D) (bf16, f16):
+    rows concentrate on a few keys, the running max moves by large steps and
+    |O| approaches the largest |v|. The bar adds to the dtype's bar the
+    rounding of O itself to the output type, half an ulp: at most 2^-8 |O|
+    (bf16) or 2^-11 |O| (f16), element by element. LSE keeps its bar."""
+    rng = np.random.default_rng(77)
+    rel = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+    for n in range(16):
+        dtype = ["bf16", "f16"][n % 2]
+        D = int(rng.choice([64, 128]))
+        H, B = int(rng.choice([1, 2])), 1
+        S = int(rng.integers(1, 700))
+        causal = bool(rng.integers(0, 3) > 0)
+        window = int(rng.integers(1, 300)) if causal and rng.random() < 0.4 else 0
+        n_sink = int(rng.integers(0, 5)) if window else 0
+        scale = float(rng.choice([1.0, -1.0]) * rng.uniform(1.5, 8.0) / math.sqrt(D))
+        q, k, v = fa_inputs.make_qkv(B, H, S, D, dtype, seed=5000 + n)
+        label = (f"sharp #{n} {dtype} H{H} S{S} D{D} c{int(causal)} w{window} s{n_sink} "
+                 f"scale {scale:+.3f}")
+        o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=scale)
+        worst_excess, worst_l = -1.0, 0.0
+        for h in range(H):
+            O, L = ORACLE.attention_fwd(fa_inputs.to_f64(q[:, h:h + 1]),
+                                        fa_inputs.to_f64(k[:, h:h + 1]),
+                                        fa_inputs.to_f64(v[:, h:h + 1]), causal=causal,
+                                        scale=scale, window=window, n_sink=n_sink)
+            og = o[0, h].float().cpu().double().numpy()
+            lg = lse[0, h].cpu().double().numpy()
+            bar = TOL_O[dtype] + rel[dtype] * np.abs(O[0, 0])
+            worst_excess = max(worst_excess, float((np.abs(og - O[0, 0]) - bar).max()))
+            worst_l = max(worst_l, float((np.abs(lg - L[0, 0]) /
+                                          np.maximum(1.0, np.abs(L[0, 0]))).max()))
+        _say(f"  {label}: max(|dO| - bar)={worst_excess:.3e}  max rel dLSE={worst_l:.3e}")
+        assert worst_excess <= 0.0, label
+        assert worst_l <= TOL_LSE_REL, label
 
 
 # --------------------------------------------------------------------------- #
