@@ -66,15 +66,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 874698547,
+     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 871053107,
     ("causal_b1h32s16384d128_bf16",
-     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 1632249446,
+     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 1660509798,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 2240363725,
+     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 2243135283,
     ("noncausal_b2h8s1024d64_f16",
-     "cefdffac4b81ebd7f40c2dd3ccbf54b9b7bd2afe3dc7e7c27461a0142ea8688c"): 9124454,
+     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 9124454,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "58f17dac447e74ac555445813dad4958c6948d9b76a9c6e425f25cf308ed2bd3"): 1870238925,
+     "f4a82705a0cf9edace35a5bbf20f9b6bb43b26f901d8cbc9d14ed92dab96e22d"): 1879993344,
 }
 
 

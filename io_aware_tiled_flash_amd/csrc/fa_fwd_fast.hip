@@ -750,8 +750,21 @@ void fa_fwd_parts_kernel(FwdParams p) {
   }
 }
 
+// Waves per SIMD the kernel is built for. At D = 128 the O accumulator, the Q
+// fragments and the scores take about 240 registers, so two waves share a SIMD
+// (two 4-wave work-groups per CU). At D = 64 the same state fits in 168, and a
+// third 4-wave work-group per CU (96 KiB of LDS in all) gives each SIMD a
+// third wave to fill the matrix cores while the other two are in their
+// softmax stretch: same-process A/B +8 % causal, +3 % unmasked, +8 % with a
+// 1024-key window. An 8-wave work-group still runs alone on its CU.
+template <int D>
+constexpr int fast_waves_per_simd() {
+  return D == 64 ? 3 : 2;
+}
+
 template <typename T, int D, int NW, int AL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
+    fast_waves_per_simd<D>(), fast_waves_per_simd<D>())))
 void fa_fwd_fast_kernel(FwdParams p) {
   constexpr int TILE = kBCf * D;
   __shared__ __attribute__((aligned(1024))) T k0s[TILE];

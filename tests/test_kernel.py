@@ -687,6 +687,22 @@ def test_alibi_slope_range_causal(dtype):
                 alibi=sl.astype(np.float64), label=f"{dtype} S{S} w{window} alibi slope range")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dim_64_full_grid(dtype):
+    """D = 64 on a grid of 512 work-groups of 128 rows (B2 H16 S2048), which
+    takes the 4-wave kernel built for three waves per SIMD rather than the
+    small-grid schedule; no mask, causal, and a window with sinks, each checked
+    on every row of three heads."""
+    assert fa.flash_attn_fwd_kernel(2, 16, 2048, 64, fa.FA_BF16).startswith(
+        "fa_fwd_fast_kernel<bf16,D=64,waves=4>")
+    q, k, v = fa_inputs.make_qkv(2, 16, 2048, 64, dtype, seed=64)
+    heads = [(0, 0), (1, 15), (1, 6)]
+    for causal, window, n_sink in ((False, 0, 0), (True, 0, 0), (True, 300, 3)):
+        o, lse = gpu_fwd(q, k, v, causal=causal, window=window, n_sink=n_sink, scale=0.125)
+        compare(o, lse, q, k, v, dtype, causal=causal, scale=0.125, window=window,
+                n_sink=n_sink, heads=heads, label=f"{dtype} D64 B2H16 S2048 c{int(causal)} w{window}")
+
+
 def test_eight_wave_work_groups():
     """The 8-wave (256-row) work-groups that long sequences use, forced on
     shorter ones: ALiBi under the causal mask (backward walk), a window with
