@@ -973,6 +973,8 @@ def test_backward_grouped_heads_alibi_scale(dtype, dkv_kernel):
     _bwd_case(1, 4, 1, 190, 64, dtype, False, 0, 0, 0.125, seed=4, label="mqa")
     _bwd_case(1, 4, 2, 230, 128, dtype, True, 0, 0, 0.088, seed=5,
               slopes=ORACLE.alibi_slopes(4), label="alibi")
+    _bwd_case(1, 4, 2, 230, 64, dtype, True, 0, 0, 0.125, seed=9,
+              slopes=ORACLE.alibi_slopes(4), label="alibi D64")
     _bwd_case(1, 2, 2, 150, 64, dtype, True, 0, 0, -0.2, seed=6, label="negative scale")
     _bwd_case(1, 2, 2, 150, 64, dtype, False, 0, 0, 0.0, seed=7, label="zero scale")
     # a window wide enough that a key block sees masked, then fully visible,
