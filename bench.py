@@ -66,15 +66,15 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 871053107,
+     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 441420800,
     ("causal_b1h32s16384d128_bf16",
-     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 1660509798,
+     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 1561507226,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 2243135283,
+     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 2243202662,
     ("noncausal_b2h8s1024d64_f16",
-     "5e74da1957e0b3bf73b020e3d714659da89ee10da749bd8a0702277c370e08d7"): 9124454,
+     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 9184870,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "f4a82705a0cf9edace35a5bbf20f9b6bb43b26f901d8cbc9d14ed92dab96e22d"): 1879993344,
+     "90e41e285024ab97a4489a25bbb77ef700af016bc5ed77d5e24635d64fdc99b0"): 1864199373,
 }
 
 

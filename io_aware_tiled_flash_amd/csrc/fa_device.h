@@ -132,31 +132,11 @@ __device__ __forceinline__ bool block_hidden(int r0, int r1, int k0, int causal,
   return window > 0 && k0 >= n_sink && k1 < r0 && r0 - k1 >= window;
 }
 
-// Work-group -> (query block, batch*head). Heaviest query blocks first under
-// the causal mask. Consecutive ids walk over heads, and the dispatcher deals
-// ids round-robin over the 8 XCDs, so with B*H a multiple of 8 every query
-// block of a head runs on one XCD; the heads are spread so that each XCD
-// holds a contiguous run of them, which keeps query heads that share a
-// key/value head (consecutive heads) on one XCD's L2 as well.
-//
-// Without the causal triangle (no mask, or a sliding window) every query
-// block costs about the same, and the order is chosen for the L2 instead:
-// each XCD takes a contiguous run of heads and walks each head's query
-// blocks in order, so the work-groups resident on an XCD at one time cover
-// one or two heads, whose keys and values fit its L2 (rank-major order would
-// spread them over every head of the XCD, and a window's keys would be
-// fetched again for each of them).
+// Work-group -> (query block, batch*head): the order wg_tile describes.
 __device__ __forceinline__ void wg_coords(const FwdParams& p, int id, int& qb, int& bh) {
-  if ((!p.causal || p.window > 0) && (p.BH & 7) == 0) {
-    const int l = id >> 3;
-    bh = (id & 7) * (p.BH >> 3) + l / p.nqb;
-    qb = l % p.nqb;
-    return;
-  }
-  const int x = id % p.BH;
-  const int rank = id / p.BH;
-  bh = (p.BH & 7) ? x : (x & 7) * (p.BH >> 3) + (x >> 3);
-  qb = p.causal ? (p.nqb - 1 - rank) : rank;
+  const Tile t = wg_tile(id, p.BH, p.nqb, p.causal != 0, p.window > 0);
+  qb = t.qb;
+  bh = t.bh;
 }
 // The work-group's position in dispatch order, or its mirror image when the
 // host asks for the reverse order (a testing aid: no work-group depends on

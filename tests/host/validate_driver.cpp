@@ -634,6 +634,54 @@ int main() {
                               (int)(rng.next() % 4), (int)(rng.next() % 2), rng.size(),
                               (int)(rng.next() % 2), &kname, &err);
   }
+  // ---- the forward work-group order ----
+  // wg_tile must visit every (query block, head) of the grid exactly once; with
+  // BH a multiple of 8 every work-group of an XCD (id & 7) must stay in that
+  // XCD's run of heads; under the causal mask each head's query blocks must
+  // come heaviest first, and the work-groups of an XCD must cover at most
+  // kOrderGroupHeads heads within any kOrderGroupHeads * nqb consecutive ids.
+  {
+    int grids = 0;
+    for (int BH : {1, 2, 3, 5, 7, 8, 16, 24, 40, 64, 96, 128, 256}) {
+      for (int nqb : {1, 2, 3, 7, 16, 32, 33, 64, 128}) {
+        for (int mode = 0; mode < 3; ++mode) {
+          const bool causal = mode > 0, window = mode == 2;
+          std::vector<int> seen((size_t)BH * nqb, 0);
+          std::vector<int> last_qb(BH, 1 << 30);
+          bool ok = true;
+          for (int id = 0; id < BH * nqb; ++id) {
+            const fa::Tile t = fa::wg_tile(id, BH, nqb, causal, window);
+            if (t.qb < 0 || t.qb >= nqb || t.bh < 0 || t.bh >= BH) { ok = false; break; }
+            ++seen[(size_t)t.bh * nqb + t.qb];
+            if (BH % 8 == 0 && t.bh / (BH / 8) != (id & 7)) ok = false;
+            if (causal && !window) {
+              if (t.qb >= last_qb[t.bh]) ok = false;   // heaviest first, per head
+              last_qb[t.bh] = t.qb;
+            }
+          }
+          for (int c : seen) ok = ok && c == 1;
+          if (ok && BH % 8 == 0 && causal && !window) {
+            // heads per XCD within each window of kOrderGroupHeads * nqb ids of that XCD
+            const int HX = BH / 8, W = fa::kOrderGroupHeads * nqb;
+            for (int xcd = 0; xcd < 8 && ok; ++xcd)
+              for (int k0 = 0; k0 < HX * nqb && ok; k0 += W) {
+                std::vector<int> heads;
+                for (int kk = k0; kk < std::min(k0 + W, HX * nqb); ++kk) {
+                  const int bh = fa::wg_tile(8 * kk + xcd, BH, nqb, true, false).bh;
+                  if (std::find(heads.begin(), heads.end(), bh) == heads.end()) heads.push_back(bh);
+                }
+                ok = (int)heads.size() <= fa::kOrderGroupHeads;
+              }
+          }
+          expect(ok, "wg_tile (BH " + std::to_string(BH) + ", nqb " + std::to_string(nqb) +
+                         ", mode " + std::to_string(mode) + ")");
+          ++grids;
+        }
+      }
+    }
+    std::printf("wg_tile: %d grids checked\n", grids);
+  }
+
   std::printf("fuzz: %d forward and %d backward calls accepted of 200000 each\n", ok_fwd, ok_bwd);
   if (g_failures) {
     std::printf("%d FAILURES\n", g_failures);
