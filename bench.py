@@ -74,7 +74,7 @@ MEASURED_TRAFFIC: dict = {
     ("noncausal_b2h8s1024d64_f16",
      "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 9184870,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "90e41e285024ab97a4489a25bbb77ef700af016bc5ed77d5e24635d64fdc99b0"): 1864199373,
+     "0849152d0c03e5be6f47102e7b82a374b0047d6bf389f4e346004a6d20947d34"): 1277349274,
 }
 
 
