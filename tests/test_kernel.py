@@ -337,6 +337,23 @@ def test_multi_batch_head_layout(dtype):
         compare(o, lse, q, k, v, dtype, causal=causal, scale=0.125, label=f"{dtype} B3H5 c{causal}")
 
 
+def test_work_group_order_uneven_groups():
+    """B*H = 40: eight XCD runs of five heads each, which the causal order splits
+    into groups of four and one. Every (query block, head) must still be
+    computed once: the small-grid schedule, the 4-wave kernel (ALiBi) and the
+    backward, all on every row against the oracle."""
+    B, H, S, D = 5, 8, 300, 128
+    q, k, v = fa_inputs.make_qkv(B, H, S, D, "bf16", seed=40)
+    sl = ORACLE.alibi_slopes(H).astype(np.float32)
+    for slopes in (None, sl):
+        sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+        o, lse = gpu_fwd(q, k, v, causal=True, scale=0.088, alibi_slopes=sd)
+        compare(o, lse, q, k, v, "bf16", causal=True, scale=0.088,
+                alibi=None if slopes is None else slopes.astype(np.float64),
+                label=f"B5H8 causal alibi={slopes is not None}")
+    _bwd_case(B, H, H, S, D, "bf16", True, 0, 0, 0.088, seed=41, label="B5H8 backward")
+
+
 # --------------------------------------------------------------------------- #
 # Stress inputs and degenerate cases
 # --------------------------------------------------------------------------- #
