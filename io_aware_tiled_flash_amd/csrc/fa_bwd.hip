@@ -487,12 +487,7 @@ void fa_bwd_dkv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int BHkv = p.BH / p.G;
-  // the order of wg_tile over key blocks. Under the causal mask the first key
-  // blocks are the heaviest, with a window too (the sink block is seen by
-  // every query block), so every causal grid takes the grouped heaviest-first
-  // order; the XCD's K/V heads go in groups of four, so the work-groups on an
-  // XCD stream the query tiles of at most four heads (L2 fetches of the
-  // headline backward 1669 -> 1061 MB, +0.4 % there, +3.9 % on B4 H32 S4096).
+  // the order of wg_tile over key blocks, as in fa_bwd_dkv2_kernel below
   const Tile tk = wg_tile((int)blockIdx.x, BHkv, p.nkb, p.causal != 0, false);
   const int bkv = tk.bh;
   const int kb = p.causal ? p.nkb - 1 - tk.qb : tk.qb;
