@@ -22,7 +22,8 @@ of up to 50 launches with an event pair each gives the per-launch spread
 launch / mean launch duration of the timed region; peak = MI355X dense
 bf16/fp16 MFMA (2516.6 TFLOP/s = 256 CU x 2.4 GHz x 4096 FLOP/clk) or fp32
 MFMA (157.3 TFLOP/s); traffic = counter-measured HBM bytes per launch when the
-kernel sources match those the counters were taken on, else null.
+launched kernel (wave count, key parts) and its sources match those the
+counters were taken on, else null.
 
 `cpu_baseline` times the fp64 CPU oracle on the same inputs: whole heads (all
 rows), fanned out over a process pool of one single-threaded worker per host
@@ -54,8 +55,9 @@ MAX_POOL = 16
 
 # HBM bytes per step measured with rocprofv3 counter runs (FETCH_SIZE scaled
 # x2.0 and WRITE_SIZE x1.0, the factors a 256 MiB device copy of known size
-# gives), keyed by workload and the SHA-256 of the kernel sources the counters
-# were taken on. Any other source tree reports traffic = null.
+# gives), keyed by workload, the kernel the host plan launches for it (wave
+# count, key parts) and the SHA-256 of the kernel sources the counters were
+# taken on. Any other plan or source tree reports traffic = null.
 FWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_fwd_fast.hip",
                "io_aware_tiled_flash_amd/csrc/fa_device.h",
                "io_aware_tiled_flash_amd/csrc/fa_shapes.h",
@@ -66,15 +68,20 @@ BWD_SOURCES = ["io_aware_tiled_flash_amd/csrc/fa_bwd.hip",
                "io_aware_tiled_flash_amd/csrc/fa_lds.h"]
 MEASURED_TRAFFIC: dict = {
     ("causal_b4h16s4096d128_bf16",
-     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 441420800,
+     "fa::fa_fwd_fast_kernel<bf16,D=128,waves=8> (256x64 tile)",
+     "cf0e7cd960b9e263fa05a241594851d179c68273fd52a28df40389910730ad31"): 373837414,
     ("causal_b1h32s16384d128_bf16",
-     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 1561507226,
+     "fa::fa_fwd_fast_kernel<bf16,D=128,waves=8> (256x64 tile)",
+     "cf0e7cd960b9e263fa05a241594851d179c68273fd52a28df40389910730ad31"): 1672267162,
     ("window1024_sink4_b8h32s8192d128_bf16",
-     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 2243202662,
+     "fa::fa_fwd_fast_kernel<bf16,D=128,waves=4> (128x64 tile)",
+     "cf0e7cd960b9e263fa05a241594851d179c68273fd52a28df40389910730ad31"): 2246306202,
     ("noncausal_b2h8s1024d64_f16",
-     "9c010ba4f053d71bf90149bc5f0626d2bfb663dfe99798ffaf151faf66c32edd"): 9184870,
+     "fa::fa_fwd_parts_kernel<f16,D=64,parts=4> (8 waves, 64x64 tile)",
+     "cf0e7cd960b9e263fa05a241594851d179c68273fd52a28df40389910730ad31"): 9184870,
     ("bwd_causal_b4h16s4096d128_bf16",
-     "b1b878f099c6e94c80c506f34af3abc3280cbf164e49d46faf192e2a3fe39f97"): 1233962598,
+     "fa::fa_bwd_dq_kernel<bf16,D=128> (128 rows, 4 waves) + fa_bwd_dkv2_kernel<bf16,D=128> (128 keys, 4 waves, 2 work-groups per CU)",
+     "db2877e197378f75ee45000ce7b7fcbd8f0c18c09ee4a7e88f69e43b6e746b22"): 1233278771,
 }
 
 
@@ -126,7 +133,7 @@ def kernel_name(fa, w) -> str:
         return "fa::" + fa.flash_attn_bwd_kernel(w.B, w.H, w.S, w.D, code, H_kv=w.kv_heads,
                                                  causal=w.causal, window=w.window, alibi=w.alibi)
     return "fa::" + fa.flash_attn_fwd_kernel(w.B, w.H, w.S, w.D, code, alibi=w.alibi,
-                                             n_split=w.n_split)
+                                             n_split=w.n_split, window=w.window)
 
 
 def nominal_flops(w) -> float:
@@ -459,7 +466,8 @@ def main():
                       "p90": round(pct(90), 2), "max": round(per[-1], 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": MEASURED_TRAFFIC.get((name, kernel_source_hash(w.backward))),
+                     "traffic": MEASURED_TRAFFIC.get((name, kernel_name(fa, w),
+                                                      kernel_source_hash(w.backward))),
                      "kernel": kernel_name(fa, w),
                      "mean_launch_us": round(mean_launch_ms * 1e3, 2)},
         "cpu_baseline": base,

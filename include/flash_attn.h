@@ -257,17 +257,18 @@ int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o,
  * flash_attn_tile_shape -- host-only query of the tile flash_attn_fwd uses for
  * a problem of this shape: *block_q query rows per work-group and *block_k keys
  * per streamed key/value block (the kernel and its work-group size are chosen
- * from B*H, S, D and dtype). With ALiBi slopes or a key split the bf16/f16
+ * from B*H, S, D, dtype and the window: window is the call's sliding window,
+ * 0 for none). With ALiBi slopes or a key split the bf16/f16
  * D=64/128 kernel never takes the small-grid schedule, whose 64-row blocks
  * (four key parts at D = 64) this query may report. Returns FA_OK,
- * FA_ERR_INVALID (NULL output, B/H/S < 1, unknown dtype) or
+ * FA_ERR_INVALID (NULL output, B/H/S < 1, window < 0, unknown dtype) or
  * FA_ERR_UNSUPPORTED (D not implemented). Touches no GPU. Tuning aids, read
  * per call when set: FLASH_ATTN_WAVES=4|8 fixes the work-group size of the
  * bf16/f16 D=64/128 kernel, FLASH_ATTN_PARTS=0|2|4 the key parts of its
  * small-grid schedule (0 = off).
  */
-int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,
-                          int* block_k);
+int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t window,
+                          int* block_q, int* block_k);
 
 /*
  * flash_attn_fwd_kernel -- host-only query of the kernel a forward call would
@@ -275,14 +276,15 @@ int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
  * template, dtype, head dim, work-group shape, tile) into the caller's host
  * buffer buf of buf_bytes bytes, truncated to fit (128 bytes always suffice).
  * alibi: nonzero when slopes are passed (flash_attn_fwd_ext); n_split: 1, or
- * the key split of flash_attn_fwd_split. Returns FA_OK, FA_ERR_INVALID (NULL
- * or empty buffer, B/H/S < 1, unknown dtype, n_split outside [1, 256]; buf
+ * the key split of flash_attn_fwd_split; window: the call's sliding window, 0
+ * for none. Returns FA_OK, FA_ERR_INVALID (NULL or empty buffer, B/H/S < 1,
+ * window < 0, unknown dtype, n_split outside [1, 256]; buf
  * then holds "") or FA_ERR_UNSUPPORTED (head dim, or a split the fast kernel
  * cannot take). Touches no GPU; honours FLASH_ATTN_WAVES and
  * FLASH_ATTN_PARTS like the calls.
  */
 int flash_attn_fwd_kernel(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
-                          int64_t n_split, char* buf, int64_t buf_bytes);
+                          int64_t n_split, int64_t window, char* buf, int64_t buf_bytes);
 
 /*
  * flash_attn_bwd_kernel -- host-only query of the two kernels flash_attn_bwd

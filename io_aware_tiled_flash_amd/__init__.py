@@ -63,9 +63,10 @@ class _CAPI:
             "flash_attn_bwd_workspace_bytes", [i64, i64, i64], i64)
         self.flash_attn_tile_shape = self._fn(
             "flash_attn_tile_shape",
-            [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
+            [i64, i64, i64, i64, i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32)
         self.flash_attn_fwd_kernel = self._fn(
-            "flash_attn_fwd_kernel", [i64, i64, i64, i64, i32, i32, i64, ctypes.c_char_p, i64], i32)
+            "flash_attn_fwd_kernel",
+            [i64, i64, i64, i64, i32, i32, i64, i64, ctypes.c_char_p, i64], i32)
         self.flash_attn_bwd_kernel = self._fn(
             "flash_attn_bwd_kernel",
             [i64, i64, i64, i64, i64, i32, i32, i64, i32, ctypes.c_char_p, i64], i32)
@@ -98,20 +99,23 @@ def flash_attn_version() -> str:
     return capi().flash_attn_version().decode()
 
 
-def flash_attn_tile_shape(B: int, H: int, S: int, D: int, dtype: int) -> tuple[int, int]:
+def flash_attn_tile_shape(B: int, H: int, S: int, D: int, dtype: int, *,
+                          window: int = 0) -> tuple[int, int]:
     """(query rows per work-group, keys per streamed block) flash_attn_fwd uses
-    for a [B, H, S, D] problem of this dtype."""
+    for a [B, H, S, D] problem of this dtype and sliding window (0: none)."""
     bq, bk = ctypes.c_int(0), ctypes.c_int(0)
-    rc = capi().flash_attn_tile_shape(B, H, S, D, dtype, ctypes.byref(bq), ctypes.byref(bk))
+    rc = capi().flash_attn_tile_shape(B, H, S, D, dtype, window, ctypes.byref(bq),
+                                      ctypes.byref(bk))
     _check(rc)
     return bq.value, bk.value
 
 
 def flash_attn_fwd_kernel(B: int, H: int, S: int, D: int, dtype: int, *, alibi: bool = False,
-                          n_split: int = 1) -> str:
+                          n_split: int = 1, window: int = 0) -> str:
     """Description of the kernel a forward call would launch for this problem."""
     buf = ctypes.create_string_buffer(128)
-    _check(capi().flash_attn_fwd_kernel(B, H, S, D, dtype, int(bool(alibi)), n_split, buf, 128))
+    _check(capi().flash_attn_fwd_kernel(B, H, S, D, dtype, int(bool(alibi)), n_split, window,
+                                        buf, 128))
     return buf.value.decode()
 
 

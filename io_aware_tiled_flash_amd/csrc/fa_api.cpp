@@ -201,21 +201,22 @@ int flash_attn_fwd_counted(const void* q, const void* k, const void* v, void* o,
   return forward(a, stream);
 }
 
-int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q,
-                          int* block_k) {
+int flash_attn_tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t window,
+                          int* block_q, int* block_k) {
   g_last_error.clear();
-  return fa::tile_shape(B, H, S, D, dtype, block_q, block_k, &g_last_error);
+  return fa::tile_shape(B, H, S, D, dtype, window, block_q, block_k, &g_last_error);
 }
 
 int flash_attn_fwd_kernel(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
-                          int64_t n_split, char* buf, int64_t buf_bytes) {
+                          int64_t n_split, int64_t window, char* buf, int64_t buf_bytes) {
   g_last_error.clear();
   if (!buf || buf_bytes < 1) {
     g_last_error = "null or empty output buffer";
     return FA_ERR_INVALID;
   }
   std::string name;
-  const int rc = fa::fwd_kernel_name(B, H, S, D, dtype, alibi, n_split, &name, &g_last_error);
+  const int rc = fa::fwd_kernel_name(B, H, S, D, dtype, alibi, n_split, window, &name,
+                                     &g_last_error);
   const size_t n = rc == FA_OK ? std::min(name.size(), (size_t)(buf_bytes - 1)) : 0;
   std::memcpy(buf, name.data(), n);
   buf[n] = '\0';

@@ -244,6 +244,6 @@ struct Plan {
   int parts;     // key parts of the small-grid schedule (2 or 4), or 0
 };
 // plain: no ALiBi and no key split (the small-grid schedule needs both).
-Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain);
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain, int64_t window);
 
 }  // namespace fa

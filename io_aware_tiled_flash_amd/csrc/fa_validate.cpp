@@ -66,12 +66,17 @@ int reverse_order() {
 }  // namespace
 
 // Kernel choice. bf16/f16 with D = 64 or 128 take the fast kernel. Its
-// work-group holds 4 waves (128 query rows), so two work-groups share a CU and
-// run out of step with each other: one's softmax (vector ALU) overlaps the
-// other's matrix products. Only for very long sequences (S >= 16384, with at
-// least two 8-wave work-groups per CU) do 8 waves win, by halving the K/V
-// tile traffic per query row. FLASH_ATTN_WAVES=4|8 overrides the wave count
-// (tuning only).
+// work-group holds 4 waves (128 query rows), so two work-groups share a CU (three
+// at D = 64) and run out of step with each other: one's softmax (vector ALU)
+// overlaps the other's matrix products. With at least two 8-wave work-groups
+// per CU, 8 waves (256 rows, one work-group per CU) halve the K/V tile traffic
+// per query row. They win for S >= 16384, and at D = 128 without a window from
+// S = 2048 on (same-process A/B with the grouped work-group order: +1.9 % on
+// causal B4 H16 S4096, +2.4 % with grouped heads, +5 % at S 2048 and
+// unmasked, +1.3 % at S 8192; -4 % at S 1024, -2.8 % with a 1024-key window,
+// -16 % with a 256-key one, -1.7 % at D = 64). window is the call's window (0,
+// or >= S, for none). FLASH_ATTN_WAVES=4|8 overrides the wave count (tuning
+// only).
 //
 // Grids of fewer than two 4-wave work-groups of 128 rows per CU (256 CUs)
 // leave SIMDs with one wave or none. Without ALiBi and a key split they take
@@ -81,7 +86,7 @@ int reverse_order() {
 // parts (D = 64, where the tiles of four parts fit in LDS) use 64-row blocks,
 // which doubles the work-group count of a grid that covers at most half the
 // CUs. FLASH_ATTN_PARTS=0|2|4 overrides (tuning).
-Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain) {
+Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain, int64_t window) {
   Plan pl;
   pl.parts = 0;
   if (fast_supported(D, dtype)) {
@@ -91,7 +96,8 @@ Plan plan_fwd(int64_t BH, int64_t S, int64_t D, int dtype, bool plain) {
     // are small, so it cannot overflow for any argument.
     const int64_t nb8 = S / 256 + (S % 256 != 0);
     const bool many8 = BH >= 512 || nb8 >= 512 || BH * nb8 >= 512;
-    pl.nw = (S >= 16384 && many8) ? 8 : 4;
+    const bool no_window = window <= 0 || window >= S;
+    pl.nw = (many8 && (S >= 16384 || (D == 128 && no_window && S >= 2048))) ? 8 : 4;
     if (const char* e = std::getenv("FLASH_ATTN_WAVES")) {
       const int v = std::atoi(e);
       if (v == 4 || v == 8) pl.nw = v;
@@ -181,7 +187,7 @@ int prepare_fwd(const FwdCall& a, FwdLaunch* out, std::string* err) {
   if (n_split > 1 && !fast_supported(D, a.dtype))
     return fail(err, FA_ERR_UNSUPPORTED,
                 "key splitting needs bf16 / f16 with head dim 64 or 128");
-  const Plan plan = plan_fwd(bh, S, D, a.dtype, !a.alibi && n_split == 1);
+  const Plan plan = plan_fwd(bh, S, D, a.dtype, !a.alibi && n_split == 1, a.window);
   const int64_t br = plan.block_q;
   const int64_t nqb = (S + br - 1) / br;
   // grid = nqb * bh * n_split work-groups (times 256 threads at most) in 32 bits;
@@ -420,23 +426,25 @@ void bwd_bind_workspace(BwdParams* p, void* ws) {
   p->lse2 = ws ? static_cast<float*>(ws) + (int64_t)p->BH * p->Sp : nullptr;
 }
 
-int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q, int* block_k,
-               std::string* err) {
+int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t window, int* block_q,
+               int* block_k, std::string* err) {
   if (!block_q || !block_k) return fail(err, FA_ERR_INVALID, "null output pointer");
   if (B < 1 || H < 1 || S < 1) return fail(err, FA_ERR_INVALID, "B, H and S must be >= 1");
+  if (window < 0) return fail(err, FA_ERR_INVALID, "window must be >= 0");
   if (elem_bytes(dtype) == 0) return fail(err, FA_ERR_INVALID, "unknown dtype");
   if (!supported_d(D)) return fail(err, FA_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
   if (B > INT64_MAX / H) return fail(err, FA_ERR_INVALID, "B*H overflows");
-  const Plan plan = plan_fwd(B * H, S, D, dtype, true);
+  const Plan plan = plan_fwd(B * H, S, D, dtype, true, window);
   *block_q = plan.block_q;
   *block_k = plan.block_k;
   return FA_OK;
 }
 
 int fwd_kernel_name(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
-                    int64_t n_split, std::string* name, std::string* err) {
+                    int64_t n_split, int64_t window, std::string* name, std::string* err) {
   if (!name) return fail(err, FA_ERR_INVALID, "null output pointer");
   if (B < 1 || H < 1 || S < 1) return fail(err, FA_ERR_INVALID, "B, H and S must be >= 1");
+  if (window < 0) return fail(err, FA_ERR_INVALID, "window must be >= 0");
   const int e = elem_bytes(dtype);
   if (e == 0) return fail(err, FA_ERR_INVALID, "unknown dtype");
   if (n_split < 1 || n_split > 256) return fail(err, FA_ERR_INVALID, "n_split must be in [1, 256]");
@@ -444,7 +452,7 @@ int fwd_kernel_name(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int a
   if (n_split > 1 && !fast_supported(D, dtype))
     return fail(err, FA_ERR_UNSUPPORTED, "key splitting needs bf16 / f16 with head dim 64 or 128");
   if (B > INT64_MAX / H) return fail(err, FA_ERR_INVALID, "B*H overflows");
-  const Plan plan = plan_fwd(B * H, S, D, dtype, !alibi && n_split == 1);
+  const Plan plan = plan_fwd(B * H, S, D, dtype, !alibi && n_split == 1, window);
   const char* ty = dtype == kDtypeF32 ? "f32" : dtype == kDtypeF16 ? "f16" : "bf16";
   const std::string d = std::to_string(D);
   const std::string tile = " (" + std::to_string(plan.block_q) + "x" + std::to_string(plan.block_k) + " tile)";

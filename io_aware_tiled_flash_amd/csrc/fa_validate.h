@@ -85,8 +85,8 @@ int64_t split_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, int64_
 int64_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t S, std::string* err);
 
 // flash_attn_tile_shape.
-int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int* block_q, int* block_k,
-               std::string* err);
+int tile_shape(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t window, int* block_q,
+               int* block_k, std::string* err);
 
 // flash_attn_bwd_kernel: writes the kernels' description to *name.
 int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, int dtype, int causal,
@@ -94,6 +94,6 @@ int bwd_kernel_name(int64_t B, int64_t H, int64_t H_kv, int64_t S, int64_t D, in
 
 // flash_attn_fwd_kernel: writes the kernel's description to *name.
 int fwd_kernel_name(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int alibi,
-                    int64_t n_split, std::string* name, std::string* err);
+                    int64_t n_split, int64_t window, std::string* name, std::string* err);
 
 }  // namespace fa

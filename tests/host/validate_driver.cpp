@@ -305,9 +305,11 @@ int main() {
     expect(fa::bwd_workspace_bytes(4, 16, 4096, &err) == 2 * 64 * 4096 * 4, "bwd ws size");
     expect(fa::bwd_workspace_bytes(1, 1, 0, &err) == -1, "bwd ws invalid");
     int bq = 0, bk = 0;
-    expect(fa::tile_shape(1, 1, 64, 48, FA_BF16, &bq, &bk, &err) == FA_ERR_UNSUPPORTED, "tile d48");
-    expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, &bq, &bk, &err) == FA_OK && bk == fa::kFastBC,
+    expect(fa::tile_shape(1, 1, 64, 48, FA_BF16, 0, &bq, &bk, &err) == FA_ERR_UNSUPPORTED, "tile d48");
+    expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, 0, &bq, &bk, &err) == FA_OK && bk == fa::kFastBC,
            "tile c3");
+    expect(fa::tile_shape(4, 16, 4096, 128, FA_BF16, -1, &bq, &bk, &err) == FA_ERR_INVALID,
+           "tile window < 0");
   }
 
   // ---- LDS layouts: every read pattern free of bank conflicts ----
@@ -625,11 +627,11 @@ int main() {
                                     &err);
     (void)fa::bwd_workspace_bytes(rng.size(), rng.size(), rng.size(), &err);
     int bq, bk;
-    (void)fa::tile_shape(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4), &bq,
-                         &bk, &err);
+    (void)fa::tile_shape(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4),
+                         rng.size(), &bq, &bk, &err);
     std::string kname;
     (void)fa::fwd_kernel_name(rng.size(), rng.size(), rng.size(), rng.size(), (int)(rng.next() % 4),
-                              (int)(rng.next() % 2), rng.size(), &kname, &err);
+                              (int)(rng.next() % 2), rng.size(), rng.size(), &kname, &err);
     (void)fa::bwd_kernel_name(rng.size(), rng.size(), rng.size(), rng.size(), rng.size(),
                               (int)(rng.next() % 4), (int)(rng.next() % 2), rng.size(),
                               (int)(rng.next() % 2), &kname, &err);

@@ -67,7 +67,9 @@ def test_small_grid_tile_choice(monkeypatch):
     """The plan behind flash_attn_tile_shape: a D = 64 grid of at most 128
     work-groups of 128 rows (half the CUs) takes four key parts on 64-row
     blocks; other grids of fewer than 512 keep 128-row blocks (two parts, or
-    8 waves at S >= 16384); FLASH_ATTN_PARTS=0|2|4 overrides."""
+    8 waves at S >= 16384); D = 128 without a window takes 8 waves from
+    S = 2048 once there are 512 such work-groups; FLASH_ATTN_PARTS=0|2|4
+    overrides."""
     monkeypatch.delenv("FLASH_ATTN_PARTS", raising=False)
     monkeypatch.delenv("FLASH_ATTN_WAVES", raising=False)
     for dt in (fa.FA_F16, fa.FA_BF16):
@@ -76,12 +78,20 @@ def test_small_grid_tile_choice(monkeypatch):
         assert fa.flash_attn_tile_shape(1, 16, 2048, 64, dt) == (128, 64)    # 256: two parts
         assert fa.flash_attn_tile_shape(1, 32, 2048, 64, dt) == (128, 64)    # 512: 4 waves
         assert fa.flash_attn_tile_shape(2, 8, 1024, 128, dt) == (128, 64)    # D = 128: two parts
-        assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt) == (128, 64)
+        assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt) == (256, 64)  # 8 waves
+        assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt, window=1024) == (128, 64)
+        assert fa.flash_attn_tile_shape(4, 16, 4096, 128, dt, window=4096) == (256, 64)
+        assert fa.flash_attn_tile_shape(4, 16, 4096, 64, dt) == (128, 64)    # D = 64: 4 waves
+        assert fa.flash_attn_tile_shape(16, 16, 1024, 128, dt) == (128, 64)  # S < 2048
+        assert fa.flash_attn_tile_shape(1, 16, 4096, 128, dt) == (128, 64)  # 256 groups of 8
         assert fa.flash_attn_tile_shape(1, 32, 16384, 128, dt) == (256, 64)  # 8 waves
+        assert fa.flash_attn_tile_shape(1, 32, 16384, 64, dt) == (256, 64)
     c2 = fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16)
     assert c2 == "fa_fwd_parts_kernel<f16,D=64,parts=4> (8 waves, 64x64 tile)", c2
     assert "parts=2" in fa.flash_attn_fwd_kernel(2, 8, 1024, 128, fa.FA_BF16)
-    assert "waves=4" in fa.flash_attn_fwd_kernel(4, 16, 4096, 128, fa.FA_BF16)
+    assert "waves=8" in fa.flash_attn_fwd_kernel(4, 16, 4096, 128, fa.FA_BF16)
+    assert "waves=8" in fa.flash_attn_fwd_kernel(4, 16, 4096, 128, fa.FA_BF16, alibi=True)
+    assert "waves=4" in fa.flash_attn_fwd_kernel(4, 16, 4096, 128, fa.FA_BF16, window=1024)
     assert "waves=8" in fa.flash_attn_fwd_kernel(1, 32, 16384, 128, fa.FA_BF16)
     # ALiBi and key splits never take the small-grid schedule
     assert "fast_kernel" in fa.flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, alibi=True)
@@ -93,8 +103,12 @@ def test_small_grid_tile_choice(monkeypatch):
         fa.flash_attn_fwd_kernel(1, 1, 64, 32, fa.FA_BF16, n_split=2)
     with pytest.raises(ValueError):
         fa.flash_attn_fwd_kernel(1, 1, 64, 64, fa.FA_BF16, n_split=0)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd_kernel(1, 1, 64, 64, fa.FA_BF16, window=-1)
+    with pytest.raises(ValueError):
+        fa.flash_attn_tile_shape(1, 1, 64, 64, fa.FA_BF16, window=-1)
     buf = ctypes.create_string_buffer(8)   # truncated to fit, NUL-terminated
-    assert fa.capi().flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, 0, 1, buf, 8) == fa.FA_OK
+    assert fa.capi().flash_attn_fwd_kernel(2, 8, 1024, 64, fa.FA_F16, 0, 1, 0, buf, 8) == fa.FA_OK
     assert buf.value == b"fa_fwd_"
     monkeypatch.setenv("FLASH_ATTN_PARTS", "0")
     assert fa.flash_attn_tile_shape(2, 8, 1024, 64, fa.FA_F16) == (128, 64)
