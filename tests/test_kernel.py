@@ -720,10 +720,31 @@ def test_head_dim_64_full_grid(dtype):
                 n_sink=n_sink, heads=heads, label=f"{dtype} D64 B2H16 S2048 c{int(causal)} w{window}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dim_128_eight_wave_plan(dtype):
+    """D = 128 without a window from S = 2048 on a grid of 512 work-groups of
+    256 rows (B4 H16 S2048): the plan takes the 8-wave kernel by itself; no
+    mask, causal, causal with grouped heads, and a ragged length (S 2100, whose
+    last block holds 52 rows), each checked on every row of three heads. A
+    window on the same grid keeps 4 waves."""
+    for dt in (fa.FA_BF16, fa.FA_F16):
+        assert "waves=8" in fa.flash_attn_fwd_kernel(4, 16, 2048, 128, dt)
+        assert "waves=8" in fa.flash_attn_fwd_kernel(4, 16, 2100, 128, dt)
+        assert "waves=4" in fa.flash_attn_fwd_kernel(4, 16, 2048, 128, dt, window=512)
+    heads = [(0, 0), (3, 15), (2, 9)]
+    for S, Hkv, causal in ((2048, 16, False), (2048, 16, True), (2048, 4, True), (2100, 16, True)):
+        q, _, _ = fa_inputs.make_qkv(4, 16, S, 128, dtype, seed=S + Hkv)
+        k, v = _kv(4, Hkv, S, 128, dtype, seed=S + Hkv + 1)
+        scale = 1.0 / math.sqrt(128)
+        o, lse = gpu_fwd(q, k, v, causal=causal, scale=scale)
+        compare(o, lse, q, k, v, dtype, causal=causal, scale=scale, heads=heads,
+                label=f"{dtype} D128 B4H16 Hkv{Hkv} S{S} c{int(causal)} (8 waves by plan)")
+
+
 def test_eight_wave_work_groups():
-    """The 8-wave (256-row) work-groups that long sequences use, forced on
-    shorter ones: ALiBi under the causal mask (backward walk), a window with
-    sinks, grouped heads and a ragged tail."""
+    """The 8-wave (256-row) work-groups that long sequences and D = 128 without
+    a window use, forced on shorter ones: ALiBi under the causal mask (backward
+    walk), a window with sinks, grouped heads and a ragged tail."""
     old = os.environ.get("FLASH_ATTN_WAVES")
     os.environ["FLASH_ATTN_WAVES"] = "8"
     try:
