@@ -81,7 +81,7 @@ MEASURED_TRAFFIC: dict = {
      "cf0e7cd960b9e263fa05a241594851d179c68273fd52a28df40389910730ad31"): 9184870,
     ("bwd_causal_b4h16s4096d128_bf16",
      "fa::fa_bwd_dq_kernel<bf16,D=128> (128 rows, 4 waves) + fa_bwd_dkv2_kernel<bf16,D=128> (128 keys, 4 waves, 2 work-groups per CU)",
-     "db2877e197378f75ee45000ce7b7fcbd8f0c18c09ee4a7e88f69e43b6e746b22"): 1233278771,
+     "35da84e324f63fb02051f45a7017d6980165b754c353cb789df7ae33507e3385"): 1227915059,
 }
 
 

@@ -828,114 +828,120 @@ void fa_bwd_dkv2_kernel(BwdParams p) {
       else
         tile_load(q0s, d0s, r0s, it + 1);
     }
-    const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
-    const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
-    const int ehi = sinkj ? big : emin + wlen - 1;
-    // The LDS offsets pass through an empty asm each step, so the read
-    // addresses are formed here (one add each) instead of being hoisted out
-    // of the loop, where 30-odd of them do not fit the register budget.
-    RowXor<D> rl = ro;
-    uint32_t vl = vo;
-    TrXor<D> tl = tro;
-    asm volatile("" : "+v"(rl.b), "+v"(vl), "+v"(tl.b[0]), "+v"(tl.b[1]));
-    auto vrow = [&](int s) __attribute__((always_inline)) { return at_bytes(vs, vl ^ (32u * s)); };
-    f32x16 sc, dp;
+    // Under the causal mask a tile whose rows all precede this wave's keys adds
+    // nothing to them (its weights are exact zeros): the wave skips its products.
+    if (!MASK || !p.causal || q0 + BQ - 1 >= k_lo + 32 * wave) {
+      const float b2 = ALIBI ? p.alibi[bh % p.H] * kLog2e : 0.f;
+      const int emin = j - q0 - 4 * h;   // keep iff e >= emin and (e < emin + wlen or sinkj)
+      const int ehi = sinkj ? big : emin + wlen - 1;
+      // The LDS offsets pass through an empty asm each step, so the read
+      // addresses are formed here (one add each) instead of being hoisted out
+      // of the loop, where 30-odd of them do not fit the register budget.
+      RowXor<D> rl = ro;
+      uint32_t vl = vo;
+      TrXor<D> tl = tro;
+      asm volatile("" : "+v"(rl.b), "+v"(vl), "+v"(tl.b[0]), "+v"(tl.b[1]));
+      auto vrow = [&](int s) __attribute__((always_inline)) {
+        return at_bytes(vs, vl ^ (32u * s));
+      };
+      f32x16 sc, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = 0.f;
-      dp[r] = 0.f;
-    }
-    // S = Q K^T (K in registers) and dP = dO V^T (dO, V from LDS), reads
-    // pinned two k-steps ahead of their MFMAs (one with ALiBi, whose bias
-    // terms need the registers): left free, the scheduler hoists every read
-    // and the kernel spills; the other work-group's wave on the SIMD covers
-    // the read latency.
-    if constexpr (!ALIBI) {
-      v8 qa[2], da[2], va[2];
-      qa[0] = lds_row8(at_bytes(qs, rl.at(0)));
-      qa[1] = lds_row8(at_bytes(qs, rl.at(1)));
-      da[0] = lds_row8(at_bytes(dos, rl.at(0)));
-      va[0] = lds_row8(vrow(0));
+      for (int r = 0; r < 16; ++r) {
+        sc[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      // S = Q K^T (K in registers) and dP = dO V^T (dO, V from LDS), reads
+      // pinned two k-steps ahead of their MFMAs (one with ALiBi, whose bias
+      // terms need the registers): left free, the scheduler hoists every read
+      // and the kernel spills; the other work-group's wave on the SIMD covers
+      // the read latency.
+      if constexpr (!ALIBI) {
+        v8 qa[2], da[2], va[2];
+        qa[0] = lds_row8(at_bytes(qs, rl.at(0)));
+        qa[1] = lds_row8(at_bytes(qs, rl.at(1)));
+        da[0] = lds_row8(at_bytes(dos, rl.at(0)));
+        va[0] = lds_row8(vrow(0));
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) {
-          da[(s + 1) & 1] = lds_row8(at_bytes(dos, rl.at(s + 1)));
-          va[(s + 1) & 1] = lds_row8(vrow(s + 1));
+        for (int s = 0; s < NS; ++s) {
+          if (s + 1 < NS) {
+            da[(s + 1) & 1] = lds_row8(at_bytes(dos, rl.at(s + 1)));
+            va[(s + 1) & 1] = lds_row8(vrow(s + 1));
+          }
+          sc = Tr::mma(qa[s & 1], kf[s], sc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s + 2 < NS) qa[s & 1] = lds_row8(at_bytes(qs, rl.at(s + 2)));
+          dp = Tr::mma(da[s & 1], va[s & 1], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        sc = Tr::mma(qa[s & 1], kf[s], sc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 2 < NS) qa[s & 1] = lds_row8(at_bytes(qs, rl.at(s + 2)));
-        dp = Tr::mma(da[s & 1], va[s & 1], dp);
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        v8 qa = lds_row8(at_bytes(qs, rl.at(0)));
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const v8 da = lds_row8(at_bytes(dos, rl.at(s))), va = lds_row8(vrow(s));
+          sc = Tr::mma(qa, kf[s], sc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s + 1 < NS) qa = lds_row8(at_bytes(qs, rl.at(s + 1)));
+          dp = Tr::mma(da, va, dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    } else {
-      v8 qa = lds_row8(at_bytes(qs, rl.at(0)));
+      // this lane's rows of the block: 8 g + 4 h + (0..3); with ALiBi their
+      // lse2 / delta are read one group of four at a time, pinned (all 32 at
+      // once ran that build out of registers)
+      const uint32_t mw = MASK ? keep_word(emin, ehi, -1, 0) : 0u;
+      f32x4 l2[4], dd[4];
+      const auto read_rows = [&](int g) {
+        l2[g] = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * h);
+        dd[g] = *reinterpret_cast<const f32x4*>(rs + 64 + 8 * g + 4 * h);
+      };
+      if constexpr (!ALIBI) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const v8 da = lds_row8(at_bytes(dos, rl.at(s))), va = lds_row8(vrow(s));
-        sc = Tr::mma(qa, kf[s], sc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < NS) qa = lds_row8(at_bytes(qs, rl.at(s + 1)));
-        dp = Tr::mma(da, va, dp);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int g = 0; g < 4; ++g) read_rows(g);
       }
-    }
-    // this lane's rows of the block: 8 g + 4 h + (0..3); with ALiBi their
-    // lse2 / delta are read one group of four at a time, pinned (all 32 at
-    // once ran that build out of registers)
-    const uint32_t mw = MASK ? keep_word(emin, ehi, -1, 0) : 0u;
-    f32x4 l2[4], dd[4];
-    const auto read_rows = [&](int g) {
-      l2[g] = *reinterpret_cast<const f32x4*>(rs + 8 * g + 4 * h);
-      dd[g] = *reinterpret_cast<const f32x4*>(rs + 64 + 8 * g + 4 * h);
-    };
-    if constexpr (!ALIBI) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) read_rows(g);
-    }
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (ALIBI) read_rows(g);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if constexpr (ALIBI) read_rows(g);
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r = 4 * g + e4;
-        const int e = 8 * g + e4;
-        float x;
-        if (ALIBI)
-          x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
-        else
-          x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
-        float pr = fast_exp2(x);
-        if (MASK) pr = keep_or(pr, mw, e, 0u);
-        sc[r] = pr;                        // P
-        dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int r = 4 * g + e4;
+          const int e = 8 * g + e4;
+          float x;
+          if (ALIBI)
+            x = __builtin_fmaf(sc[r], p.c, -b2 * fabsf((float)(e - emin))) - l2[g][e4];
+          else
+            x = __builtin_fmaf(sc[r], p.c, -l2[g][e4]);
+          float pr = fast_exp2(x);
+          if (MASK) pr = keep_or(pr, mw, e, 0u);
+          sc[r] = pr;                        // P
+          dp[r] = pr * (dp[r] - dd[g][e4]);  // dS
+        }
+        if constexpr (ALIBI) __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (ALIBI) __builtin_amdgcn_sched_barrier(0);
-    }
-    // P and dS as MFMA B operands (16 rows each half); the fp32 tiles die here
-    const v8 pb[2] = {pack8<T>(sc, 0), pack8<T>(sc, 1)};
-    const v8 db[2] = {pack8<T>(dp, 0), pack8<T>(dp, 1)};
-    __builtin_amdgcn_sched_barrier(0);
-    // dV^T += dO^T P and dK^T += Q^T dS: per (16-row half u, 32-wide d tile)
-    // the two transposed operands, one pair ahead of its MFMAs
-    auto tr_reads = [&](int u, int dt, v8& o, v8& q) __attribute__((always_inline)) {
-      const T* qq = qs + 16 * u * D;
-      const T* oo = dos + 16 * u * D;
-      o = lds_tr8(at_bytes(oo, tl.lo(dt)), at_bytes(oo, tl.hi(dt)));
-      q = lds_tr8(at_bytes(qq, tl.lo(dt)), at_bytes(qq, tl.hi(dt)));
-    };
-    v8 oT, qT;
-    tr_reads(0, 0, oT, qT);
-#pragma unroll
-    for (int x = 0; x < 2 * NDT; ++x) {
-      const int u = x / NDT, dt = x % NDT;
-      v8 on = oT, qn = qT;
-      if (x + 1 < 2 * NDT) tr_reads((x + 1) / NDT, (x + 1) % NDT, on, qn);
-      dv[dt] = Tr::mma(oT, pb[u], dv[dt]);
-      dk[dt] = Tr::mma(qT, db[u], dk[dt]);
+      // P and dS as MFMA B operands (16 rows each half); the fp32 tiles die here
+      const v8 pb[2] = {pack8<T>(sc, 0), pack8<T>(sc, 1)};
+      const v8 db[2] = {pack8<T>(dp, 0), pack8<T>(dp, 1)};
       __builtin_amdgcn_sched_barrier(0);
-      oT = on;
-      qT = qn;
+      // dV^T += dO^T P and dK^T += Q^T dS: per (16-row half u, 32-wide d tile)
+      // the two transposed operands, one pair ahead of its MFMAs
+      auto tr_reads = [&](int u, int dt, v8& o, v8& q) __attribute__((always_inline)) {
+        const T* qq = qs + 16 * u * D;
+        const T* oo = dos + 16 * u * D;
+        o = lds_tr8(at_bytes(oo, tl.lo(dt)), at_bytes(oo, tl.hi(dt)));
+        q = lds_tr8(at_bytes(qq, tl.lo(dt)), at_bytes(qq, tl.hi(dt)));
+      };
+      v8 oT, qT;
+      tr_reads(0, 0, oT, qT);
+#pragma unroll
+      for (int x = 0; x < 2 * NDT; ++x) {
+        const int u = x / NDT, dt = x % NDT;
+        v8 on = oT, qn = qT;
+        if (x + 1 < 2 * NDT) tr_reads((x + 1) / NDT, (x + 1) % NDT, on, qn);
+        dv[dt] = Tr::mma(oT, pb[u], dv[dt]);
+        dk[dt] = Tr::mma(qT, db[u], dk[dt]);
+        __builtin_amdgcn_sched_barrier(0);
+        oT = on;
+        qT = qn;
+      }
     }
     wait_vmem<0>();
     __syncthreads();
